@@ -1,0 +1,286 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module is shared by the oracle side and the GPU side of every test and by
+the benchmark. It holds no part of the method's arithmetic: no dot products, no
+softmax, no slot or block lookups, no quantization of the kind the kernels do.
+It only draws random numbers and lays them out with the shapes, distributions
+and structure of the workloads:
+
+  * per-sequence context lengths (fixed or uniform in a range),
+  * a random order of physical block ids (the pool's initial free list; the
+    allocation itself is the block manager's job, see the block-table builders),
+  * Gaussian queries / keys / values rounded to bf16 by round-to-nearest-even
+    (numpy on the host, or torch on a device for the large workloads),
+  * NaN poison for memory that no sequence owns, so any stray read shows up,
+  * for quantized caches, codes drawn by torch's own fp8/int8 casts of scaled
+    Gaussians (a library routine independent of both the oracle's and the
+    kernels' quantizers) together with per-(block, head) fp32 scales.
+
+Workload recipes follow the five configurations of the decode-attention study
+(tiny MHA, Llama-3-8B layer, Llama-3-70B layer, long-context with sinks, and
+quantized KV with a shared prefix); the shapes come from the pages'
+KV-layout discussion ("9 Decode and KV Cache", sections 9.3-9.5) and the SoK
+paper's Llama-3-70B running example (section 1.2).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+# dtype tags used across the repository's Python code (kept in sync with the
+# C headers by value, not by import: 0 f32, 1 bf16, 2 fp8 e4m3 (OCP), 3 int8)
+F32, BF16, FP8, INT8 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", INT8: "int8"}
+ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1, INT8: 1}
+BF16_NAN = np.uint16(0x7FC0)
+FP8_NAN = np.uint8(0x7F)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and structure of one decode-attention workload."""
+    name: str
+    seed: int
+    B: int
+    n_q: int
+    n_kv: int
+    d_h: int
+    block_size: int
+    kv_dtype: int
+    q_dtype: int
+    ctx_lo: int            # context lengths (incl. the token appended this step)
+    ctx_hi: int            # uniform integer in [ctx_lo, ctx_hi]
+    pool_blocks: Optional[int] = None  # None: exactly the blocks needed
+    free_fraction: float = 0.0         # extra free (poisoned) blocks in the pool
+    sink_tokens: int = 0               # K rows at logical positions < sink_tokens ...
+    sink_factor: float = 1.0           # ... are multiplied by this (exact in bf16)
+    shared_prefix_tokens: int = 0      # first tokens' blocks shared by all rows
+    scale: Optional[float] = None      # softmax scale; None -> 1/sqrt(d_h)
+
+    @property
+    def g(self) -> int:
+        return self.n_q // self.n_kv
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(self.scale) if self.scale is not None else 1.0 / math.sqrt(self.d_h)
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the study (shapes from the pages; recipe in the design doc).
+TINY_MHA = Workload("tiny_mha", 1, B=1, n_q=4, n_kv=4, d_h=64, block_size=16,
+                    kv_dtype=F32, q_dtype=F32, ctx_lo=256, ctx_hi=256, pool_blocks=32)
+LLAMA8B_LAYER = Workload("llama3_8b_layer", 2, B=32, n_q=32, n_kv=8, d_h=128, block_size=16,
+                         kv_dtype=BF16, q_dtype=BF16, ctx_lo=512, ctx_hi=4096,
+                         scale=1.0 / math.sqrt(128))
+LLAMA70B_LAYER = Workload("llama3_70b_layer_b8_32k", 3, B=8, n_q=64, n_kv=8, d_h=128,
+                          block_size=16, kv_dtype=BF16, q_dtype=BF16, ctx_lo=32768,
+                          ctx_hi=32768, free_fraction=0.10)
+LONG_SINKS = Workload("long_context_131k_sinks", 4, B=1, n_q=64, n_kv=8, d_h=128,
+                      block_size=16, kv_dtype=BF16, q_dtype=BF16, ctx_lo=131072,
+                      ctx_hi=131072, sink_tokens=4, sink_factor=8.0)
+QUANT_PREFIX_FP8 = Workload("quant_prefix_fp8", 5, B=64, n_q=32, n_kv=8, d_h=128,
+                            block_size=16, kv_dtype=FP8, q_dtype=BF16, ctx_lo=1024,
+                            ctx_hi=16384, shared_prefix_tokens=2048)
+QUANT_PREFIX_INT8 = QUANT_PREFIX_FP8.with_(name="quant_prefix_int8", seed=6, kv_dtype=INT8)
+
+WORKLOADS = {w.name: w for w in (TINY_MHA, LLAMA8B_LAYER, LLAMA70B_LAYER, LONG_SINKS,
+                                 QUANT_PREFIX_FP8, QUANT_PREFIX_INT8)}
+
+
+# ---------------------------------------------------------------- primitives
+def rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns by round-to-nearest-even (input dtype conversion,
+    done the standard way: add 0x7FFF plus the kept LSB, keep the high half).
+    NaN inputs map to the canonical bf16 NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    r[np.isnan(x)] = BF16_NAN
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 (exact widening)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def context_lengths(w: Workload, r: np.random.Generator) -> np.ndarray:
+    if w.ctx_lo == w.ctx_hi:
+        return np.full(w.B, w.ctx_lo, dtype=np.int32)
+    return r.integers(w.ctx_lo, w.ctx_hi + 1, size=w.B).astype(np.int32)
+
+
+def blocks_needed(ctx: np.ndarray, block_size: int) -> np.ndarray:
+    """Number of logical blocks each row occupies (ceil division of its length)."""
+    return (np.asarray(ctx, dtype=np.int64) + block_size - 1) // block_size
+
+
+def pool_size(w: Workload, ctx: np.ndarray) -> int:
+    need = int(blocks_needed(ctx, w.block_size).sum())
+    if w.shared_prefix_tokens:
+        # shared blocks are stored once; every row's private blocks are extra
+        sp = w.shared_prefix_tokens // w.block_size
+        nb = blocks_needed(ctx, w.block_size)
+        need = sp + int(np.sum(nb - np.minimum(sp, nb - 1)))
+    if w.pool_blocks is not None:
+        return max(int(w.pool_blocks), need)
+    if w.free_fraction > 0:
+        return int(math.ceil(need / (1.0 - w.free_fraction)))
+    return need
+
+
+def free_order(num_blocks: int, r: np.random.Generator) -> np.ndarray:
+    """A random permutation of physical block ids: the pool's initial free list.
+    Drawing it here (rather than inside the pool) keeps the allocator's
+    placement reproducible on both sides from one seeded input."""
+    return r.permutation(num_blocks).astype(np.int32)
+
+
+@dataclasses.dataclass
+class HostInputs:
+    """Host (numpy) inputs of one decode step."""
+    w: Workload
+    ctx: np.ndarray             # [B] int32, context lengths incl. the new token
+    num_blocks: int
+    free_order: np.ndarray      # [num_blocks] int32 permutation
+    shared_ids_count: int       # number of shared prefix blocks (0 if none)
+    q: np.ndarray               # [B, n_q, d_h] raw (float32 or uint16 bf16 bits)
+    k_cache: np.ndarray         # [NB, n_kv, bs, d_h] raw (float32 / uint16 / uint8 / int8)
+    v_cache: np.ndarray
+    k_scale: Optional[np.ndarray] = None   # [NB, n_kv] float32 (quantized only)
+    v_scale: Optional[np.ndarray] = None
+    k_new: Optional[np.ndarray] = None     # [B, n_kv, d_h] raw, the step's new K
+    v_new: Optional[np.ndarray] = None
+
+
+def gaussian(shape, dtype: int, r: np.random.Generator) -> np.ndarray:
+    """N(0,1) samples in the storage form of `dtype` (fp32, or bf16 bits)."""
+    x = r.standard_normal(size=shape, dtype=np.float32)
+    if dtype == F32:
+        return x
+    if dtype == BF16:
+        return bf16_bits_from_f32(x)
+    raise ValueError("gaussian(): only f32 / bf16 storage")
+
+
+def raw_dtype(dtype: int):
+    return {F32: np.float32, BF16: np.uint16, FP8: np.uint8, INT8: np.int8}[dtype]
+
+
+def make_host_inputs(w: Workload, seed: Optional[int] = None, with_new: bool = True) -> HostInputs:
+    """Draw every random input of one decode step of workload `w` on the host.
+
+    The cache is filled with N(0,1) everywhere; which blocks and slots end up
+    owned by a sequence is decided by the block-table builder from
+    `free_order`, after which `poison_unowned` marks the rest as NaN.
+    """
+    r = rng(w.seed if seed is None else seed)
+    ctx = context_lengths(w, r)
+    nb = pool_size(w, ctx)
+    order = free_order(nb, r)
+    q = gaussian((w.B, w.n_q, w.d_h), w.q_dtype, r)
+    shape = (nb, w.n_kv, w.block_size, w.d_h)
+    ks = vs = None
+    if w.kv_dtype in (F32, BF16):
+        kc = gaussian(shape, w.kv_dtype, r)
+        vc = gaussian(shape, w.kv_dtype, r)
+    else:
+        kc, ks = quantized_gaussian(shape, w.kv_dtype, r)
+        vc, vs = quantized_gaussian(shape, w.kv_dtype, r)
+    kn = vn = None
+    if with_new:
+        src = BF16 if w.kv_dtype != F32 else F32
+        kn = gaussian((w.B, w.n_kv, w.d_h), src, r)
+        vn = gaussian((w.B, w.n_kv, w.d_h), src, r)
+    sp = w.shared_prefix_tokens // w.block_size if w.shared_prefix_tokens else 0
+    return HostInputs(w, ctx, nb, order, sp, q, kc, vc, ks, vs, kn, vn)
+
+
+def quantized_gaussian(shape, dtype: int, r: np.random.Generator):
+    """Codes + per-(block, head) scales for N(0,1) data stored 8-bit.
+
+    scale = amax over the (block, head) tile / qmax (448 for fp8 e4m3, 127 for
+    int8); codes come from torch's own casts of x/scale (float8_e4m3fn cast,
+    or round + clamp for int8), a library path that neither the oracle nor the
+    kernels use.
+    """
+    import torch
+    x = r.standard_normal(size=shape, dtype=np.float32)
+    amax = np.abs(x).max(axis=(2, 3))
+    qmax = 448.0 if dtype == FP8 else 127.0
+    scale = np.where(amax > 0, amax / qmax, 1.0).astype(np.float32)
+    y = torch.from_numpy(x / scale[:, :, None, None])
+    y = y.clamp(-qmax, qmax)
+    if dtype == FP8:
+        codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    else:
+        codes = torch.round(y).clamp(-127, 127).to(torch.int8).numpy().copy()
+    return codes, scale
+
+
+def apply_sinks(w: Workload, k_cache: np.ndarray, block_table: np.ndarray) -> None:
+    """Multiply the K rows of logical positions < w.sink_tokens by w.sink_factor
+    (in place, all KV heads). Positions are located through the given table;
+    a power-of-two factor is exact in bf16/fp32."""
+    if not w.sink_tokens:
+        return
+    for b in range(block_table.shape[0]):
+        for t in range(w.sink_tokens):
+            pb = int(block_table[b, t // w.block_size])
+            off = t % w.block_size
+            if w.kv_dtype == BF16:
+                vals = bf16_bits_to_f32(k_cache[pb, :, off, :]) * np.float32(w.sink_factor)
+                k_cache[pb, :, off, :] = bf16_bits_from_f32(vals)
+            elif w.kv_dtype == F32:
+                k_cache[pb, :, off, :] *= np.float32(w.sink_factor)
+            else:
+                raise ValueError("sinks are defined for f32/bf16 caches")
+
+
+def poison_unowned(w: Workload, k_cache, v_cache, block_table: np.ndarray, ctx: np.ndarray,
+                   k_scale=None, v_scale=None) -> None:
+    """Fill blocks no row references, and slots past each row's length in its
+    last block, with NaN (fp32/bf16/fp8) so a stray read poisons the output.
+    int8 has no NaN: unowned blocks get NaN scales and tail slots code -128."""
+    nb = k_cache.shape[0]
+    owned = np.zeros(nb, dtype=bool)
+    bs = w.block_size
+    for b in range(block_table.shape[0]):
+        n = int(ctx[b])
+        nblk = (n + bs - 1) // bs
+        ids = block_table[b, :nblk]
+        owned[ids] = True
+    free = ~owned
+    nan = {F32: np.float32(np.nan), BF16: BF16_NAN, FP8: FP8_NAN, INT8: np.int8(-128)}[w.kv_dtype]
+    k_cache[free] = nan
+    v_cache[free] = nan
+    if k_scale is not None:
+        k_scale[free] = np.float32(np.nan)
+        v_scale[free] = np.float32(np.nan)
+    for b in range(block_table.shape[0]):
+        n = int(ctx[b])
+        if n % bs:
+            pb = int(block_table[b, (n - 1) // bs])
+            # a shared block is never a row's last block, so this cannot
+            # clobber another row's data
+            k_cache[pb, :, n % bs:, :] = nan
+            v_cache[pb, :, n % bs:, :] = nan
+
+
+# ----------------------------------------------------- device (torch) inputs
+def device_gaussian_bf16(shape, gen, device):
+    """N(0,1) bf16 tensor drawn on `device` with a seeded torch generator; the
+    fp32 -> bf16 cast is torch's round-to-nearest-even."""
+    import torch
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
