@@ -1,0 +1,15 @@
+"""Paged single-token decode attention for AMD MI355X (gfx950).
+
+The C library libpda (include/pda.h) holds the block pool, the block-table
+builder and the HIP kernels (KV append, quantized append, paged decode
+attention over bf16 / fp32 / fp8 / int8 caches, split-KV log-sum-exp merge).
+This package is its thin ctypes binding; see `binding` for the calls.
+"""
+from .binding import (  # noqa: F401
+    AttnDesc, KvDesc, NoSpace, PdaError, Pool, EXPORTS, LIB_PATH,
+    F32, BF16, FP8_E4M3, INT8,
+    version, last_error, dtype_code,
+    kv_append, kv_append_quant,
+    attn_desc, attn_workspace_size, attn_plan, workspace_for,
+    paged_decode_attn, paged_decode_attn_quant, lse_merge,
+)

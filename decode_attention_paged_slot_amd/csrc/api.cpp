@@ -1,0 +1,378 @@
+// api.cpp -- the C ABI: argument validation, split planning and dispatch.
+// Every device call is one or two kernel launches on the caller's stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "pda.h"
+#include "pda_internal.h"
+
+namespace pda {
+
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+thread_local char g_err[512] = "";
+
+namespace {
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int32_t hip_fail(const char* what, hipError_t e) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return PDA_EHIP;
+}
+
+bool debug_mode() {
+    const char* v = std::getenv("PDA_DEBUG");
+    return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !v[0]) return dflt;
+    return std::atoi(v);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+// Split-KV plan. The grid is (P, heads, B) with one workgroup of 4 waves per
+// cell; aim at ~2048 workgroups (8 per compute unit on a 256-CU MI355X) with
+// 32..256 blocks per partition, so every wave streams at least 8 blocks and
+// the partial results stay below 1% of the cache bytes.
+Plan make_plan(const pda_attn_desc& d) {
+    const int64_t max_ctx = std::max<int64_t>(d.max_context, 1);
+    const int32_t nblk_max =
+        (int32_t)std::min<int64_t>(ceil_div(max_ctx, d.block_size), d.max_blocks_per_seq);
+    Plan p{1, std::max(nblk_max, 1)};
+    if (d.num_partitions == 1 || nblk_max <= 1) return p;
+    int32_t bpp;
+    if (d.num_partitions > 1) {
+        bpp = ceil_div(nblk_max, d.num_partitions);
+    } else {
+        const int64_t heads = d.kv_dtype == PDA_F32 ? d.n_q : d.n_kv;   // grid.y of the kernel
+        const int64_t ctx_blocks = d.total_context > 0 ? ceil_div(d.total_context, d.block_size)
+                                                       : (int64_t)d.B * nblk_max;
+        const int64_t tiles = ctx_blocks * heads;
+        const int target = env_int("PDA_TARGET_WORKGROUPS", 2048);
+        bpp = ceil_div(tiles, std::max(target, 1));
+        bpp = std::max(bpp, env_int("PDA_MIN_BLOCKS_PER_PARTITION", 32));
+        bpp = std::min(bpp, 256);
+        bpp = (bpp + 3) & ~3;
+        const int forced = env_int("PDA_BLOCKS_PER_PARTITION", 0);
+        if (forced > 0) bpp = forced;
+    }
+    bpp = std::max(bpp, ceil_div(nblk_max, kMaxPartitions));
+    p.bpp = std::max(bpp, 1);
+    p.P = ceil_div(nblk_max, p.bpp);
+    if (p.P <= 1) p = Plan{1, std::max(nblk_max, 1)};
+    return p;
+}
+
+WsLayout ws_layout(const pda_attn_desc& d, const Plan& p) {
+    WsLayout w{0, 0, 0};
+    if (p.P <= 1) return w;
+    const size_t rows = (size_t)d.B * d.n_q;
+    w.part_o_off = 0;
+    w.part_ml_off = align256(rows * p.P * d.d_h * sizeof(float));
+    w.bytes = w.part_ml_off + align256(rows * p.P * 2 * sizeof(float));
+    return w;
+}
+
+}  // namespace pda
+
+using namespace pda;
+
+namespace {
+
+int32_t check_attn_desc(const pda_attn_desc* d, bool quant) {
+    if (!d) {
+        set_error("attention descriptor is NULL");
+        return PDA_EINVAL;
+    }
+    if (d->B < 0 || d->n_q <= 0 || d->n_kv <= 0 || d->n_q % d->n_kv != 0) {
+        set_error("bad head counts: B=%d n_q=%d n_kv=%d", d->B, d->n_q, d->n_kv);
+        return PDA_EINVAL;
+    }
+    const int g = d->n_q / d->n_kv;
+    if (g > 16) {
+        set_error("group factor %d > 16 unsupported", g);
+        return PDA_EINVAL;
+    }
+    if (d->d_h != 64 && d->d_h != 128) {
+        set_error("d_h=%d unsupported (64 or 128)", d->d_h);
+        return PDA_EINVAL;
+    }
+    if (d->block_size != kBlockSize) {
+        set_error("block_size=%d unsupported (16)", d->block_size);
+        return PDA_EINVAL;
+    }
+    if (d->max_blocks_per_seq <= 0 || d->num_blocks <= 0 || d->max_context < 0 ||
+        d->num_partitions < 0 || d->total_context < 0) {
+        set_error("bad sizes: max_blocks_per_seq=%d num_blocks=%d max_context=%d",
+                  d->max_blocks_per_seq, d->num_blocks, d->max_context);
+        return PDA_EINVAL;
+    }
+    const bool kv_ok = quant ? (d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8)
+                             : (d->kv_dtype == PDA_F32 || d->kv_dtype == PDA_BF16);
+    if (!kv_ok) {
+        set_error("kv_dtype %d not valid for this call", d->kv_dtype);
+        return PDA_EINVAL;
+    }
+    if ((d->q_dtype != PDA_F32 && d->q_dtype != PDA_BF16) ||
+        (d->out_dtype != PDA_F32 && d->out_dtype != PDA_BF16)) {
+        set_error("q_dtype / out_dtype must be F32 or BF16");
+        return PDA_EINVAL;
+    }
+    if ((int64_t)d->B * d->max_blocks_per_seq > INT32_MAX ||
+        (int64_t)d->num_blocks * d->n_kv * kBlockSize * d->d_h * 4 > ((int64_t)1 << 46)) {
+        set_error("sizes overflow the supported range");
+        return PDA_EINVAL;
+    }
+    return PDA_OK;
+}
+
+// PDA_DEBUG: validate block table and lengths on the host before launching.
+int32_t debug_check(const pda_attn_desc* d, const int32_t* block_table,
+                    const int32_t* context_lens, hipStream_t s) {
+    std::vector<int32_t> lens((size_t)d->B), table((size_t)d->B * d->max_blocks_per_seq);
+    hipError_t e = hipMemcpyAsync(lens.data(), context_lens, lens.size() * 4,
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(table.data(), block_table, table.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail("PDA_DEBUG copy", e);
+    for (int32_t b = 0; b < d->B; ++b) {
+        const int32_t n = lens[(size_t)b];
+        if (n < 0 || (int64_t)n > (int64_t)d->max_blocks_per_seq * kBlockSize) {
+            set_error("row %d: context length %d outside [0, %lld]", b, n,
+                      (long long)d->max_blocks_per_seq * kBlockSize);
+            return PDA_EINVAL;
+        }
+        for (int32_t i = 0; i < (n + kBlockSize - 1) / kBlockSize; ++i) {
+            const int32_t pb = table[(size_t)b * d->max_blocks_per_seq + i];
+            if (pb < 0 || pb >= d->num_blocks) {
+                set_error("row %d: logical block %d is unmapped (entry %d)", b, i, pb);
+                return PDA_EINVAL;
+            }
+        }
+    }
+    return PDA_OK;
+}
+
+int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                 const float* v_scale, const int32_t* block_table, const int32_t* context_lens,
+                 float scale, void* out, const pda_attn_desc* d, void* workspace,
+                 size_t ws_bytes, void* stream, bool quant) {
+    int32_t rc = check_attn_desc(d, quant);
+    if (rc != PDA_OK) return rc;
+    if (d->B == 0) return PDA_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
+        (quant && (!k_scale || !v_scale))) {
+        set_error("NULL device pointer");
+        return PDA_EINVAL;
+    }
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) {
+        set_error("q, caches and out must be 16-byte aligned");
+        return PDA_EINVAL;
+    }
+    if (!std::isfinite(scale)) {
+        set_error("scale is not finite");
+        return PDA_EINVAL;
+    }
+    const Plan plan = make_plan(*d);
+    const WsLayout ws = ws_layout(*d, plan);
+    if (ws.bytes > 0 && (!workspace || ws_bytes < ws.bytes || !aligned16(workspace))) {
+        set_error("workspace of %zu bytes needed (got %zu)", ws.bytes, ws_bytes);
+        return PDA_EWORKSPACE;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (debug_mode()) {
+        rc = debug_check(d, block_table, context_lens, s);
+        if (rc != PDA_OK) return rc;
+    }
+    AttnArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.part_o = ws.bytes ? (float*)((char*)workspace + ws.part_o_off) : nullptr;
+    a.part_ml = ws.bytes ? (float*)((char*)workspace + ws.part_ml_off) : nullptr;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.B = d->B;
+    a.n_q = d->n_q;
+    a.n_kv = d->n_kv;
+    a.g = d->n_q / d->n_kv;
+    a.d_h = d->d_h;
+    a.max_blocks = d->max_blocks_per_seq;
+    a.num_blocks = d->num_blocks;
+    a.kv_dtype = d->kv_dtype;
+    a.q_dtype = d->q_dtype;
+    a.out_dtype = d->out_dtype;
+    a.P = plan.P;
+    a.bpp = plan.bpp;
+    hipError_t e = d->kv_dtype == PDA_F32 ? launch_attn_f32(a, s) : launch_attn_mfma(a, s);
+    if (e != hipSuccess) return hip_fail("attention launch", e);
+    if (plan.P > 1) {
+        e = launch_merge_for_attn(a, s);
+        if (e != hipSuccess) return hip_fail("merge launch", e);
+    }
+    return PDA_OK;
+}
+
+int32_t check_kv_desc(const pda_kv_desc* d, bool quant) {
+    if (!d || d->n_kv <= 0 || (d->d_h != 64 && d->d_h != 128) || d->block_size != kBlockSize ||
+        d->num_blocks <= 0) {
+        set_error("bad KV descriptor");
+        return PDA_EINVAL;
+    }
+    if (quant) {
+        if ((d->cache_dtype != PDA_FP8_E4M3 && d->cache_dtype != PDA_INT8) ||
+            (d->src_dtype != PDA_F32 && d->src_dtype != PDA_BF16)) {
+            set_error("quantized append: cache FP8_E4M3/INT8, source F32/BF16");
+            return PDA_EINVAL;
+        }
+    } else if ((d->cache_dtype != PDA_F32 && d->cache_dtype != PDA_BF16) ||
+               d->src_dtype != d->cache_dtype) {
+        set_error("append: cache F32/BF16 and source of the same dtype");
+        return PDA_EINVAL;
+    }
+    return PDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pda_version(void) { return "pda 0.1.0 (gfx950)"; }
+
+const char* pda_last_error(void) { return pda::g_err; }
+
+int32_t pda_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache, const pda_kv_desc* d,
+                      void* stream) {
+    int32_t rc = check_kv_desc(d, false);
+    if (rc != PDA_OK) return rc;
+    if (num_tokens < 0) {
+        set_error("num_tokens < 0");
+        return PDA_EINVAL;
+    }
+    if (num_tokens == 0) return PDA_OK;
+    if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) {
+        set_error("NULL device pointer");
+        return PDA_EINVAL;
+    }
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) {
+        set_error("K/V buffers must be 16-byte aligned");
+        return PDA_EINVAL;
+    }
+    AppendArgs a{k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, nullptr, nullptr,
+                 d->n_kv, d->d_h, d->block_size, d->num_blocks, d->cache_dtype, d->src_dtype};
+    hipError_t e = launch_append(a, (hipStream_t)stream);
+    return e == hipSuccess ? PDA_OK : hip_fail("append launch", e);
+}
+
+int32_t pda_kv_append_quant(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                            int32_t num_tokens, void* k_cache, void* v_cache,
+                            const float* k_scale, const float* v_scale, const pda_kv_desc* d,
+                            void* stream) {
+    int32_t rc = check_kv_desc(d, true);
+    if (rc != PDA_OK) return rc;
+    if (num_tokens < 0) {
+        set_error("num_tokens < 0");
+        return PDA_EINVAL;
+    }
+    if (num_tokens == 0) return PDA_OK;
+    if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale) {
+        set_error("NULL device pointer");
+        return PDA_EINVAL;
+    }
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) {
+        set_error("K/V buffers must be 16-byte aligned");
+        return PDA_EINVAL;
+    }
+    AppendArgs a{k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, k_scale, v_scale,
+                 d->n_kv, d->d_h, d->block_size, d->num_blocks, d->cache_dtype, d->src_dtype};
+    hipError_t e = launch_append_quant(a, (hipStream_t)stream);
+    return e == hipSuccess ? PDA_OK : hip_fail("quantized append launch", e);
+}
+
+int32_t pda_attn_workspace_size(const pda_attn_desc* d, size_t* bytes) {
+    if (!bytes) {
+        set_error("bytes is NULL");
+        return PDA_EINVAL;
+    }
+    const bool quant = d && (d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8);
+    int32_t rc = check_attn_desc(d, quant);
+    if (rc != PDA_OK) return rc;
+    *bytes = ws_layout(*d, make_plan(*d)).bytes;
+    return PDA_OK;
+}
+
+int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
+                      int32_t* blocks_per_partition) {
+    if (!num_partitions || !blocks_per_partition) {
+        set_error("NULL output pointer");
+        return PDA_EINVAL;
+    }
+    const bool quant = d && (d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8);
+    int32_t rc = check_attn_desc(d, quant);
+    if (rc != PDA_OK) return rc;
+    const Plan p = make_plan(*d);
+    *num_partitions = p.P;
+    *blocks_per_partition = p.bpp;
+    return PDA_OK;
+}
+
+int32_t pda_paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens, float scale,
+                              void* out, const pda_attn_desc* d, void* workspace,
+                              size_t ws_bytes, void* stream) {
+    return run_attn(q, k_cache, v_cache, nullptr, nullptr, block_table, context_lens, scale, out,
+                    d, workspace, ws_bytes, stream, false);
+}
+
+int32_t pda_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* block_table, const int32_t* context_lens,
+                                    float scale, void* out, const pda_attn_desc* d,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+    return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
+                    d, workspace, ws_bytes, stream, true);
+}
+
+int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,
+                      int32_t d_h, float* out, void* stream) {
+    if (rows < 0 || P < 1 || P > kMaxPartitions || (d_h != 64 && d_h != 128)) {
+        set_error("pda_lse_merge: rows >= 0, 1 <= P <= %d, d_h 64 or 128", kMaxPartitions);
+        return PDA_EINVAL;
+    }
+    if (rows == 0) return PDA_OK;
+    if (!part_o || !part_ml || !out) {
+        set_error("NULL device pointer");
+        return PDA_EINVAL;
+    }
+    hipError_t e = launch_lse_merge(part_o, part_ml, rows, P, d_h, out, (hipStream_t)stream);
+    return e == hipSuccess ? PDA_OK : hip_fail("merge launch", e);
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// dtype codes, equal to pda_dtype
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT8 = 3 };
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Split x into bf16 hi (truncation) and bf16 lo (truncation of the exact
+// remainder): x - hi - lo is below 2^-16 |x|. Returns the two bf16 bit
+// patterns in the low halves.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+    const uint32_t u = __float_as_uint(x) & 0xFFFF0000u;
+    const float r = x - __uint_as_float(u);       // exact
+    hi = u >> 16;
+    lo = __float_as_uint(r) >> 16;
+}
+
+// fp32 -> OCP E4M3 code, round to nearest even with saturation to +-448.
+// NaN -> 0x7F; the sign of y is kept (so -0 -> 0x80).
+__device__ __forceinline__ uint32_t quant_fp8_e4m3(float y) {
+    const uint32_t u = __float_as_uint(y);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7Fu;
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = __uint_as_float(u & 0x7FFFFFFFu);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {
+        // subnormal range: value = m * 2^-9, m = 0..8 (m = 8 is the smallest
+        // normal, whose code is also 8)
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -6..8
+        const float mul = __uint_as_float((uint32_t)(127 + 3 - e) << 23); // 2^(3-e)
+        const float t = a * mul - 8.0f;                                   // exact, in [0, 8)
+        code = (uint32_t)((e + 7) << 3) + (uint32_t)__builtin_rintf(t);  // carry = next exponent
+    }
+    return code | sign;
+}
+
+// fp32 -> symmetric int8 code: round half to even, clamp to [-127, 127]; NaN -> 0.
+__device__ __forceinline__ int32_t quant_int8(float y) {
+    if (y != y) return 0;
+    const float r = __builtin_rintf(y);
+    return (int32_t)fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
+// Two fp32 values holding exact bf16 values -> packed bf16x2 (lo, hi).
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// 4 fp8 codes (one dword) -> 4 bf16 (two dwords), exact.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    u32x2 r;
+    r.x = __builtin_bit_cast(uint32_t, a);
+    r.y = __builtin_bit_cast(uint32_t, b);
+    return r;
+}
+
+// 4 int8 codes (one dword) -> 4 bf16 (two dwords), exact (|code| <= 128).
+__device__ __forceinline__ u32x2 int8x4_to_bf16x4(uint32_t w) {
+    const float f0 = (float)(int32_t)(int8_t)(w & 0xFFu);
+    const float f1 = (float)(int32_t)(int8_t)((w >> 8) & 0xFFu);
+    const float f2 = (float)(int32_t)(int8_t)((w >> 16) & 0xFFu);
+    const float f3 = (float)(int32_t)(int8_t)(w >> 24);
+    u32x2 r;
+    r.x = pack_bf16_trunc(f0, f1);
+    r.y = pack_bf16_trunc(f2, f3);
+    return r;
+}
+
+}  // namespace pda

@@ -1,0 +1,65 @@
+// pda_internal.h -- host-side declarations shared by the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pda.h"
+
+namespace pda {
+
+void set_error(const char* fmt, ...);
+
+// Split-KV plan: P partitions of `bpp` logical blocks each.
+struct Plan {
+    int32_t P;
+    int32_t bpp;
+};
+Plan make_plan(const pda_attn_desc& d);
+
+// Workspace layout for a plan.
+struct WsLayout {
+    size_t part_o_off, part_ml_off, bytes;
+};
+WsLayout ws_layout(const pda_attn_desc& d, const Plan& p);
+
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    const int64_t* slots;
+    int32_t T;
+    void* k_cache;
+    void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    int32_t n_kv, d_h, bs, num_blocks, cache_dtype, src_dtype;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_quant(const AppendArgs& a, hipStream_t s);
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    void* out;
+    float* part_o;   // [B][n_q][P][d_h]  (split runs only)
+    float* part_ml;  // [B][n_q][P][2]
+    float scale_log2;  // softmax scale * log2(e)
+    int32_t B, n_q, n_kv, g, d_h, max_blocks, num_blocks;
+    int32_t kv_dtype, q_dtype, out_dtype;
+    int32_t P, bpp;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,
+                            int32_t d_h, float* out, hipStream_t s);
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxPartitions = 2048;
+constexpr int kAttnThreads = 256;
+
+}  // namespace pda

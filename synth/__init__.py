@@ -284,3 +284,114 @@ def device_gaussian_bf16(shape, gen, device):
     fp32 -> bf16 cast is torch's round-to-nearest-even."""
     import torch
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+@dataclasses.dataclass
+class DeviceInputs:
+    """Device (torch) inputs of one decode step; block tables are built by the
+    caller (the oracle's pool model in tests, the library's pool in the
+    benchmark) from `free_order`."""
+    w: Workload
+    ctx: np.ndarray
+    num_blocks: int
+    free_order: np.ndarray
+    shared_ids_count: int
+    q: "object"
+    k_cache: "object"
+    v_cache: "object"
+    k_scale: "object" = None
+    v_scale: "object" = None
+    k_new: "object" = None
+    v_new: "object" = None
+
+
+def _device_quantized(shape, dtype: int, gen, device):
+    """Codes and per-(block, head) scales of N(0,1) data, with torch's casts."""
+    import torch
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    amax = x.abs().amax(dim=(2, 3))
+    qmax = 448.0 if dtype == FP8 else 127.0
+    scale = torch.where(amax > 0, amax / qmax, torch.ones_like(amax)).float()
+    y = (x / scale[:, :, None, None]).clamp_(-qmax, qmax)
+    del x
+    if dtype == FP8:
+        codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        codes = torch.round(y).clamp_(-127, 127).to(torch.int8)
+    return codes, scale
+
+
+def make_device_inputs(w: Workload, device, seed: Optional[int] = None,
+                       with_new: bool = True) -> DeviceInputs:
+    """Draw one decode step's inputs of workload `w` directly in device memory
+    (torch's seeded Philox generator; bf16 by torch's round-to-nearest-even
+    cast). Lengths and the free-list order come from numpy as on the host."""
+    import torch
+    s = w.seed if seed is None else seed
+    r = rng(s)
+    ctx = context_lengths(w, r)
+    nb = pool_size(w, ctx)
+    order = free_order(nb, r)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(s)
+    qdt = torch.bfloat16 if w.q_dtype == BF16 else torch.float32
+    q = torch.randn((w.B, w.n_q, w.d_h), generator=gen, device=device).to(qdt)
+    shape = (nb, w.n_kv, w.block_size, w.d_h)
+    ks = vs = None
+    if w.kv_dtype in (F32, BF16):
+        kdt = torch.bfloat16 if w.kv_dtype == BF16 else torch.float32
+        k = torch.randn(shape, generator=gen, device=device).to(kdt)
+        v = torch.randn(shape, generator=gen, device=device).to(kdt)
+    else:
+        k, ks = _device_quantized(shape, w.kv_dtype, gen, device)
+        v, vs = _device_quantized(shape, w.kv_dtype, gen, device)
+    kn = vn = None
+    if with_new:
+        ndt = torch.float32 if w.kv_dtype == F32 else torch.bfloat16
+        kn = torch.randn((w.B, w.n_kv, w.d_h), generator=gen, device=device).to(ndt)
+        vn = torch.randn((w.B, w.n_kv, w.d_h), generator=gen, device=device).to(ndt)
+    sp = w.shared_prefix_tokens // w.block_size if w.shared_prefix_tokens else 0
+    return DeviceInputs(w, ctx, nb, order, sp, q, k, v, ks, vs, kn, vn)
+
+
+def poison_unowned_device(w: Workload, inp: DeviceInputs, block_table: np.ndarray) -> None:
+    """Device counterpart of `poison_unowned` (NaN in unowned blocks and in the
+    tail slots of each row's last block; int8: NaN scales / code -128)."""
+    import torch
+    dev = inp.k_cache.device
+    bs = w.block_size
+    owned = np.zeros(inp.num_blocks, dtype=bool)
+    for b in range(block_table.shape[0]):
+        nblk = (int(inp.ctx[b]) + bs - 1) // bs
+        owned[block_table[b, :nblk]] = True
+    free = torch.from_numpy(np.nonzero(~owned)[0]).to(dev)
+    if w.kv_dtype == F32:
+        nan = float("nan")
+    elif w.kv_dtype == BF16:
+        nan = float("nan")
+    elif w.kv_dtype == FP8:
+        nan = 0x7F
+    else:
+        nan = -128
+    if free.numel():
+        inp.k_cache[free] = nan
+        inp.v_cache[free] = nan
+        if inp.k_scale is not None:
+            inp.k_scale[free] = float("nan")
+            inp.v_scale[free] = float("nan")
+    for b in range(block_table.shape[0]):
+        n = int(inp.ctx[b])
+        if n % bs:
+            pb = int(block_table[b, (n - 1) // bs])
+            inp.k_cache[pb, :, n % bs:, :] = nan
+            inp.v_cache[pb, :, n % bs:, :] = nan
+
+
+def apply_sinks_device(w: Workload, inp: DeviceInputs, block_table: np.ndarray) -> None:
+    """Device counterpart of `apply_sinks` (power-of-two factor: exact)."""
+    if not w.sink_tokens:
+        return
+    for b in range(block_table.shape[0]):
+        for t in range(w.sink_tokens):
+            pb = int(block_table[b, t // w.block_size])
+            inp.k_cache[pb, :, t % w.block_size, :] *= w.sink_factor

@@ -9,6 +9,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# Build what is missing (the checker and the library are compiled in-tree; a
+# GPU machine receives the built files with the tree and never rebuilds here).
+from oracle import build as _oracle_build  # noqa: E402
+from decode_attention_paged_slot_amd import build as _pda_build  # noqa: E402
+
+_oracle_build.ensure_built()
+if not os.path.exists(_pda_build.LIB):
+    _pda_build.build()
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
