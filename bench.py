@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for paged single-token decode attention on MI355X.
+
+One step = one decode step of one attention layer over a whole batch: the
+step's new K/V rows are appended into their mapped cache slots, then every
+sequence's query attends over its paged cache (split-KV partitions and their
+log-sum-exp merge included). Inputs are seeded synthetic tensors drawn in HBM
+before the timed region; nothing is copied between host and device inside it.
+
+Default workload: the Llama-3-70B layer shape on one GPU -- batch 8, 64 query
+heads over 8 KV heads (GQA g = 8), d_h 128, bf16 cache, every context 32,768
+tokens, block size 16, physical blocks placed at random in a pool with 10%
+free (NaN-poisoned) blocks. The byte counts follow the SoK paper's appendix
+A.1 accounting (cache read once, no score spill) in decimal units (appendix
+C.2).
+
+Printed: one JSON line with the metric (KV GB/s of the step), ms/step,
+the roofline object of the attention call (algorithmic bytes per launch over
+its HIP-event-timed average duration against 8 TB/s), and the CPU baseline
+(the fp64 oracle on the host's cores over the same workload). The oracle
+output is also compared with the GPU output row by row (parity at full size).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure (decimal GB/s)
+DEFAULT_WORKLOAD = "llama3_70b_layer_b8_32k"
+
+
+def _say(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-oracle", action="store_true",
+                    help="skip the CPU oracle leg (parity + cpu_baseline)")
+    ap.add_argument("--no-probe", action="store_true", help="skip the stream-copy probe")
+    ap.add_argument("--num-partitions", type=int, default=0,
+                    help="split-KV partitions (0 = the library's choice)")
+    return ap.parse_args(argv)
+
+
+def build_inputs(w, dev):
+    """Seeded device inputs, the product's block table, poison and sinks."""
+    import torch  # noqa: F401
+    import synth
+    import decode_attention_paged_slot_amd as pda
+
+    inp = synth.make_device_inputs(w, dev)
+    bs = w.block_size
+    max_blocks = int(synth.blocks_needed(inp.ctx, bs).max())
+    pool = pda.Pool(inp.num_blocks, inp.free_order)
+    shared = pool.alloc(inp.shared_ids_count) if inp.shared_ids_count else np.empty(0, np.int32)
+    table, slots = pool.build_block_table(inp.ctx, bs, max_blocks, shared)
+    synth.apply_sinks_device(w, inp, table)
+    synth.poison_unowned_device(w, inp, table)
+    return inp, pool, shared, table, slots
+
+
+def oracle_leg(w, inp, table, slots, shared, host):
+    """fp64 oracle over the whole workload on the host cores.
+
+    The oracle's inputs are the seeded cache as drawn (copied to the host
+    before any library kernel touched it), the step's new rows placed by the
+    oracle's own append, and block tables from the oracle's own pool model
+    (checked equal to the library's). Returns (timing dict, oracle out)."""
+    import oracle
+    import synth
+
+    opool = oracle.OraclePool(inp.num_blocks, inp.free_order)
+    osh = opool.alloc(inp.shared_ids_count) if inp.shared_ids_count else []
+    otable, oslots = opool.build_block_table(inp.ctx, w.block_size, table.shape[1], osh)
+    tables_equal = bool((otable == table).all() and (oslots == slots).all()
+                        and list(osh) == [int(x) for x in shared])
+    k = oracle.kv_append(host["k"], host["kn_raw"], oslots) if w.kv_dtype in (0, 1) else \
+        oracle.kv_append_quant(host["k"], host["ks"], host["kn_f32"], oslots, w.kv_dtype)
+    v = oracle.kv_append(host["v"], host["vn_raw"], oslots) if w.kv_dtype in (0, 1) else \
+        oracle.kv_append_quant(host["v"], host["vs"], host["vn_f32"], oslots, w.kv_dtype)
+    t0 = time.perf_counter()
+    out, _, _, bad = oracle.paged_attn(host["q"], k, v, otable, inp.ctx, w.softmax_scale,
+                                       n_q=w.n_q, n_kv=w.n_kv, q_dtype=w.q_dtype,
+                                       kv_dtype=w.kv_dtype, k_scale=host.get("ks"),
+                                       v_scale=host.get("vs"))
+    secs = time.perf_counter() - t0
+    del k, v
+    return {"secs": secs, "threads": oracle.num_threads(), "bad_rows": bad,
+            "tables_equal": tables_equal}, out
+
+
+def host_snapshot(w, inp):
+    """Host copies of the drawn inputs (raw storage) for the oracle leg."""
+    import torch
+    import synth
+
+    def raw(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    h = {"q": raw(inp.q), "k": raw(inp.k_cache), "v": raw(inp.v_cache)}
+    kn, vn = raw(inp.k_new), raw(inp.v_new)
+    h["kn_raw"], h["vn_raw"] = kn, vn
+    if w.kv_dtype in (2, 3):
+        h["ks"], h["vs"] = inp.k_scale.cpu().numpy(), inp.v_scale.cpu().numpy()
+        h["kn_f32"] = synth.bf16_bits_to_f32(kn)
+        h["vn_f32"] = synth.bf16_bits_to_f32(vn)
+    return h
+
+
+def stream_probe(dev, nbytes=2 << 30, reps=10):
+    """Device copy of `nbytes` (torch's copy kernel): read + write GB/s."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode path "
+                          "shards over sequences / KV heads with no exchange, and one GPU's "
+                          "throughput is the figure reported (--gpus 1)"}), flush=True)
+        return 2
+
+    import torch
+    import synth
+    import decode_attention_paged_slot_amd as pda
+    from decode_attention_paged_slot_amd import accounting as acc
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        return 2
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.workload not in synth.WORKLOADS:
+        print(json.dumps({"error": f"unknown workload {args.workload}",
+                          "known": sorted(synth.WORKLOADS)}), flush=True)
+        return 2
+    w = synth.WORKLOADS[args.workload]
+    quant = w.kv_dtype in (synth.FP8, synth.INT8)
+
+    _say(f"[bench] workload {w.name}: drawing inputs")
+    inp, pool, shared, table, slots = build_inputs(w, dev)
+    host = None if args.no_oracle else host_snapshot(w, inp)
+
+    bt = torch.from_numpy(table).to(dev)
+    cl = torch.from_numpy(inp.ctx).to(dev)
+    sl = torch.from_numpy(slots).to(dev)
+    out = torch.empty((w.B, w.n_q, w.d_h), dtype=torch.float32, device=dev)
+    desc = pda.attn_desc(inp.q, inp.k_cache, bt, max_context=int(inp.ctx.max()),
+                         kv_dtype=w.kv_dtype, num_partitions=args.num_partitions,
+                         total_context=int(inp.ctx.sum()))
+    P, bpp = pda.attn_plan(desc)
+    ws = pda.workspace_for(desc, dev)
+    scale = w.softmax_scale
+
+    if quant:
+        def append():
+            pda.kv_append_quant(inp.k_new, inp.v_new, sl, inp.k_cache, inp.v_cache,
+                                inp.k_scale, inp.v_scale, cache_dtype=w.kv_dtype)
+
+        def attend():
+            pda.paged_decode_attn_quant(inp.q, inp.k_cache, inp.v_cache, inp.k_scale,
+                                        inp.v_scale, bt, cl, scale, out, desc=desc,
+                                        workspace=ws)
+    else:
+        def append():
+            pda.kv_append(inp.k_new, inp.v_new, sl, inp.k_cache, inp.v_cache)
+
+        def attend():
+            pda.paged_decode_attn(inp.q, inp.k_cache, inp.v_cache, bt, cl, scale, out,
+                                  desc=desc, workspace=ws)
+
+    _say(f"[bench] plan P={P} blocks/partition={bpp}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        append()
+        attend()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    _say(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        append()
+        ev[i][1].record()
+        attend()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    att_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_per_step = wall * 1e3 / K
+
+    sb = acc.step_bytes(inp.ctx, n_q=w.n_q, n_kv=w.n_kv, d_h=w.d_h, block_size=w.block_size,
+                        kv_dtype=w.kv_dtype, q_dtype=w.q_dtype,
+                        new_dtype=synth.BF16 if w.kv_dtype != synth.F32 else synth.F32,
+                        shared_prefix_blocks=inp.shared_ids_count)
+    att_avg = float(np.mean(att_ms))
+    achieved = sb.attention / (att_avg * 1e-3) / 1e9
+    value = sb.step / (ms_per_step * 1e-3) / 1e9
+    _say(f"[bench] attention avg {att_avg * 1e3:.1f} us  -> {achieved:.0f} GB/s; "
+         f"step {ms_per_step * 1e3:.1f} us")
+
+    # parity of this very run's output at full size, and the CPU baseline
+    parity = None
+    cpu = None
+    if host is not None:
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(w.B * w.n_q, w.d_h).astype(np.float64)
+        _say("[bench] oracle leg (fp64, host cores)")
+        info, ref = oracle_leg(w, inp, table, slots, shared, host)
+        tol = 3e-2 if quant else 5e-3
+        err = float(np.abs(got - ref).max()) if np.isfinite(got).all() else float("inf")
+        parity = {"rows": int(ref.shape[0]), "max_abs_err": err, "tol": tol,
+                  "pass": bool(err < tol and info["bad_rows"] == 0 and info["tables_equal"]),
+                  "block_tables_identical": info["tables_equal"]}
+        cpu = {"value": round(sb.attention / info["secs"] / 1e9, 4), "unit": "GB/s",
+               "cores": int(info["threads"]), "kind": "oracle",
+               "sample": (f"whole workload ({w.B} sequences x {w.n_q} query heads, "
+                          f"{int(inp.ctx.sum())} cached tokens); fp64 two-pass oracle, "
+                          f"{info['secs']:.2f} s wall on {info['threads']} threads")}
+        _say(f"[bench] parity max-abs {err:.3g} (tol {tol}); oracle {info['secs']:.2f} s")
+
+    probe = None if args.no_probe else stream_probe(dev)
+
+    res = {
+        "metric": "decode-attn KV GB/s (% MI355X HBM peak) + us/step, 70B-shape batch 8x32k",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == synth.BF16 else synth.DTYPE_NAMES[w.kv_dtype],
+        "data": "synthetic (seeded N(0,1) q/K/V in HBM, random block placement)",
+        "config": {
+            "workload": w.name, "B": w.B, "n_q": w.n_q, "n_kv": w.n_kv, "d_h": w.d_h,
+            "block_size": w.block_size, "kv_dtype": synth.DTYPE_NAMES[w.kv_dtype],
+            "context_min": int(inp.ctx.min()), "context_max": int(inp.ctx.max()),
+            "total_context": int(inp.ctx.sum()), "pool_blocks": int(inp.num_blocks),
+            "num_partitions": P, "blocks_per_partition": bpp, "parallelism": "none (1 GPU)",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "us_per_step": {"wall_mean": round(ms_per_step * 1e3, 2),
+                        "append_median": round(_pct(app_ms, 50) * 1e3, 2),
+                        "attention_median": round(_pct(att_ms, 50) * 1e3, 2),
+                        "attention_p10": round(_pct(att_ms, 10) * 1e3, 2),
+                        "attention_p90": round(_pct(att_ms, 90) * 1e3, 2)},
+        "bytes_per_step": {"attention": sb.attention, "attention_unique": sb.attention_unique,
+                           "step": sb.step, "kv_read": sb.kv_read},
+        "roofline": {"bound": "hbm", "kernel": "paged_decode_attn (attention + merge)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "stream_copy_probe_GBps": None if probe is None else round(probe, 1),
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if (parity is None or parity["pass"]) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

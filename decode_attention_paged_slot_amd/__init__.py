@@ -4,12 +4,28 @@ The C library libpda (include/pda.h) holds the block pool, the block-table
 builder and the HIP kernels (KV append, quantized append, paged decode
 attention over bf16 / fp32 / fp8 / int8 caches, split-KV log-sum-exp merge).
 This package is its thin ctypes binding; see `binding` for the calls.
+
+The binding is loaded on first use of any of its names, so that the build
+module (`decode_attention_paged_slot_amd.build`) can be imported before the
+library exists. Using the binding without a built libpda.so raises ImportError:
+there is no fallback implementation.
 """
-from .binding import (  # noqa: F401
-    AttnDesc, KvDesc, NoSpace, PdaError, Pool, EXPORTS, LIB_PATH,
-    F32, BF16, FP8_E4M3, INT8,
-    version, last_error, dtype_code,
-    kv_append, kv_append_quant,
-    attn_desc, attn_workspace_size, attn_plan, workspace_for,
-    paged_decode_attn, paged_decode_attn_quant, lse_merge,
+import importlib
+
+_BINDING_NAMES = (
+    "AttnDesc", "KvDesc", "NoSpace", "PdaError", "Pool", "EXPORTS", "LIB_PATH",
+    "F32", "BF16", "FP8_E4M3", "INT8",
+    "version", "last_error", "dtype_code",
+    "kv_append", "kv_append_quant",
+    "attn_desc", "attn_workspace_size", "attn_plan", "workspace_for",
+    "paged_decode_attn", "paged_decode_attn_quant", "lse_merge",
 )
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        binding = importlib.import_module(".binding", __name__)
+        return getattr(binding, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
