@@ -371,6 +371,10 @@ int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, i
         set_error("NULL device pointer");
         return PDA_EINVAL;
     }
+    if (!aligned16(part_o) || !aligned16(out) || ((uintptr_t)part_ml & 7u) != 0) {
+        set_error("part_o and out must be 16-byte aligned, part_ml 8-byte aligned");
+        return PDA_EINVAL;
+    }
     hipError_t e = launch_lse_merge(part_o, part_ml, rows, P, d_h, out, (hipStream_t)stream);
     return e == hipSuccess ? PDA_OK : hip_fail("merge launch", e);
 }

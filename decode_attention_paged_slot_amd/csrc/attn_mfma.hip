@@ -73,6 +73,14 @@ __device__ __forceinline__ int lds_off(int t, int cb) {
 
 __device__ __forceinline__ uint4 ld16(const char* p) { return *(const uint4*)p; }
 
+// Streaming 16-B load of cache data: every K/V byte is read exactly once per
+// step, so the load is marked non-temporal and does not displace reusable
+// lines (block table, queries) from the caches.
+__device__ __forceinline__ uint4 ld16_stream(const char* p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float fshfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
 template <int KV>
@@ -222,9 +230,9 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_attn_mfma(AttnArgs a) {
             const char* kt = kbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
             const char* vt = vbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16(kt + col * T::ROWB + 64 * l + 16 * grp);
+            for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16_stream(kt + col * T::ROWB + 64 * l + 16 * grp);
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l) vr[s][l] = ld16(vt + 1024 * l + 16 * lane);
+            for (int l = 0; l < T::LOADS; ++l) vr[s][l] = ld16_stream(vt + 1024 * l + 16 * lane);
         };
 
         auto consume = [&](int s, int i, bool refill) {

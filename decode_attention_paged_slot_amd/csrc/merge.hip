@@ -8,8 +8,8 @@
 // of the attention step (SoK paper appendices A.1, C.4).
 //
 // One workgroup per output row: a block-wide max and sum over the partials'
-// statistics, then S = 256 / d_h slices of the partials, each reduced over
-// d_h lanes, combined through LDS.
+// statistics, then a weighted sum of the partial outputs split over
+// partition subsets, combined through LDS.
 #include "device_common.h"
 #include "pda_internal.h"
 
@@ -42,6 +42,13 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // context_lens != nullptr: row r belongs to sequence r / n_q and uses the
 // partitions its length needs (ceil(ceil(n / 16) / bpp), capped at P);
 // otherwise all P partials are read and l_p == 0 marks an empty one.
+//
+// Phase 1: every thread takes partitions p = tid, tid + 256, ... for the
+// block-wide max M and the weights w_p = l_p 2^(m_p - M), kept in LDS.
+// Phase 2: thread (sub, c) accumulates the 4-float column group c of the
+// partials p = sub, sub + SUB, ... (loads are unconditional, so they can all
+// be in flight together; an empty partial's weight is 0 and its data unused);
+// the SUB partial sums are added through LDS.
 template <int HD>
 __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -49,10 +56,11 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
                                                     int32_t n_q, int32_t P, int32_t bpp,
                                                     int32_t max_blocks, void* out,
                                                     int32_t out_dtype) {
-    constexpr int S = kThreads / HD;
+    constexpr int V = HD / 4;          // float4 column groups per row
+    constexpr int SUB = kThreads / V;  // partition subsets
     __shared__ float wsh[kMaxPartitions];
     __shared__ float red[4];
-    __shared__ float acc_sh[kThreads];
+    __shared__ f32x4 acc_sh[SUB][V];
     const int64_t row = blockIdx.x;
     int np = P;
     bool row_bad = false;
@@ -65,41 +73,47 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
     const float* ml = part_ml + row * (int64_t)P * 2;
     float mloc = -__builtin_inff();
     for (int p = threadIdx.x; p < np; p += kThreads) {
-        const float l = ml[2 * p + 1];
-        if (l != 0.0f) mloc = fmaxf(mloc, ml[2 * p]);
+        const float2 x = *(const float2*)(ml + 2 * p);
+        if (x.y != 0.0f) mloc = fmaxf(mloc, x.x);
     }
     const float M = block_max(mloc, red);
     float lsum = 0.0f;
     for (int p = threadIdx.x; p < np; p += kThreads) {
-        const float l = ml[2 * p + 1];
-        const float w = l == 0.0f ? 0.0f : l * __builtin_amdgcn_exp2f(ml[2 * p] - M);
+        const float2 x = *(const float2*)(ml + 2 * p);
+        const float w = x.y == 0.0f ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
         wsh[p] = w;
         lsum += w;
     }
-    const float L = block_sum(lsum, red);   // also orders the wsh writes
-    const int s = threadIdx.x / HD, d = threadIdx.x % HD;
-    const float* po = part_o + row * (int64_t)P * HD + d;
-    float a0 = 0.0f, a1 = 0.0f;
-    int p = s;
-    for (; p + S < np; p += 2 * S) {
-        const float w0 = wsh[p], w1 = wsh[p + S];
-        if (w0 != 0.0f) a0 += w0 * po[(int64_t)p * HD];
-        if (w1 != 0.0f) a1 += w1 * po[(int64_t)(p + S) * HD];
+    const float L = block_sum(lsum, red);   // its barriers also publish wsh
+    const int c = threadIdx.x % V, sub = threadIdx.x / V;
+    const f32x4* po = (const f32x4*)(part_o + row * (int64_t)P * HD) + c;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int p = sub; p < np; p += SUB) {
+        const f32x4 o = po[(int64_t)p * V];
+        const float w = wsh[p];
+        if (w != 0.0f) acc += w * o;
     }
-    if (p < np) {
-        const float w0 = wsh[p];
-        if (w0 != 0.0f) a0 += w0 * po[(int64_t)p * HD];
-    }
-    acc_sh[threadIdx.x] = a0 + a1;
+    acc_sh[sub][c] = acc;
     __syncthreads();
-    if (s == 0) {
-        float tot = 0.0f;
+    if (sub == 0) {
+        f32x4 tot = acc_sh[0][c];
 #pragma unroll
-        for (int k = 0; k < S; ++k) tot += acc_sh[k * HD + d];
-        float r = L != 0.0f ? tot / L : 0.0f;
-        if (row_bad) r = __builtin_nanf("");
-        if (out_dtype == DT_F32) ((float*)out)[row * HD + d] = r;
-        else ((uint16_t*)out)[row * HD + d] = (uint16_t)f32_to_bf16_rne(r);
+        for (int k = 1; k < SUB; ++k) tot += acc_sh[k][c];
+        f32x4 r;
+        const bool inv_ok = L != 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = inv_ok ? tot[e] / L : 0.0f;
+        if (row_bad) r = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                               __builtin_nanf("")};
+        if (out_dtype == DT_F32) {
+            *((f32x4*)((float*)out + row * HD) + c) = r;
+        } else {
+            uint2 h;
+            h.x = f32_to_bf16_rne(r[0]) | (f32_to_bf16_rne(r[1]) << 16);
+            h.y = f32_to_bf16_rne(r[2]) | (f32_to_bf16_rne(r[3]) << 16);
+            *((uint2*)((uint16_t*)out + row * HD) + c) = h;
+        }
     }
 }
 

@@ -260,7 +260,8 @@ int32_t pda_paged_decode_attn_quant(const void* q, const void* k_cache, const vo
  * is zero. Used inside pda_paged_decode_attn, and exported so partials from
  * several devices holding disjoint token ranges of one sequence (context
  * parallelism, section 9.7) can be merged.
- *   part_o, part_ml, out device; out float [rows][d_h] (d_h 64 or 128). */
+ *   part_o, part_ml, out device; out float [rows][d_h] (d_h 64 or 128);
+ *   part_o and out 16-byte aligned, part_ml 8-byte aligned (else EINVAL). */
 int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,
                       int32_t d_h, float* out, void* stream);
 
