@@ -133,22 +133,60 @@ def host_snapshot(w, inp):
 
 
 def stream_probe(dev, nbytes=2 << 30, reps=10):
-    """Device copy of `nbytes` (torch's copy kernel): read + write GB/s."""
+    """Streaming scale-copy b = 2 a over `nbytes` (torch's elementwise kernel):
+    read + write GB/s. The same dispatches calibrate the HBM byte counters
+    (each reads and writes exactly `nbytes`)."""
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     b = torch.empty_like(a)
-    b.copy_(a)
+    torch.mul(a, 2.0, out=b)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        b.copy_(a)
+        torch.mul(a, 2.0, out=b)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     del a, b
     torch.cuda.empty_cache()
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+# Sources whose code decides what the attention call moves; a counter summary
+# under profiles/ is only used while they hash to the value it records.
+ATTN_SOURCES = ("attn_mfma.hip", "attn_f32.hip", "merge.hip", "device_common.h",
+                "pda_internal.h", "api.cpp")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_paged_slot_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention call from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE passes, calibrated),
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"paged_decode_attn__{workload}__pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    try:
+        if fields.get("source_sha256") != attn_source_hash():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main(argv=None) -> int:
@@ -333,8 +371,9 @@ def main(argv=None) -> int:
                            "step": sb.step, "kv_read": sb.kv_read},
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attn (attention + merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
-        "stream_copy_probe_GBps": None if probe is None else round(probe, 1),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name)},
+        "stream_scale_copy_probe_GBps": None if probe is None else round(probe, 1),
         "parity": parity,
         "cpu_baseline": cpu,
     }
