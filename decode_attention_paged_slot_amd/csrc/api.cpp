@@ -51,41 +51,84 @@ void set_error(const char* fmt, ...) {
     va_end(ap);
 }
 
-// Split-KV plan. The grid is (P, heads, B) with one workgroup of 4 waves per
-// cell; aim at ~2048 workgroups (8 per compute unit on a 256-CU MI355X) with
-// 32..256 blocks per partition, so every wave streams at least 8 blocks and
-// the partial results stay below 1% of the cache bytes.
-Plan make_plan(const pda_attn_desc& d) {
+// Partition plan (fp32 caches). The grid is (P, n_q, B) with one workgroup
+// of 4 waves per cell; aim at ~2048 workgroups with 32..256 blocks per
+// partition, so every wave streams at least 8 blocks and the partial results
+// stay below 1% of the cache bytes.
+Plan make_partition_plan(const pda_attn_desc& d) {
     const int64_t max_ctx = std::max<int64_t>(d.max_context, 1);
     const int32_t nblk_max =
         (int32_t)std::min<int64_t>(ceil_div(max_ctx, d.block_size), d.max_blocks_per_seq);
-    Plan p{1, std::max(nblk_max, 1)};
+    Plan p{1, std::max(nblk_max, 1), 0, 0, 0};
     if (d.num_partitions == 1 || nblk_max <= 1) return p;
     int32_t bpp;
     if (d.num_partitions > 1) {
         bpp = ceil_div(nblk_max, d.num_partitions);
     } else {
-        const int64_t heads = d.kv_dtype == PDA_F32 ? d.n_q : d.n_kv;   // grid.y of the kernel
         const int64_t ctx_blocks = d.total_context > 0 ? ceil_div(d.total_context, d.block_size)
                                                        : (int64_t)d.B * nblk_max;
-        const int64_t tiles = ctx_blocks * heads;
-        const int target = env_int("PDA_TARGET_WORKGROUPS", 2048);
-        bpp = ceil_div(tiles, std::max(target, 1));
-        bpp = std::max(bpp, env_int("PDA_MIN_BLOCKS_PER_PARTITION", 32));
+        const int64_t tiles = ctx_blocks * d.n_q;
+        bpp = ceil_div(tiles, 2048);
+        bpp = std::max(bpp, 32);
         bpp = std::min(bpp, 256);
         bpp = (bpp + 3) & ~3;
-        const int forced = env_int("PDA_BLOCKS_PER_PARTITION", 0);
-        if (forced > 0) bpp = forced;
     }
     bpp = std::max(bpp, ceil_div(nblk_max, kMaxPartitions));
     p.bpp = std::max(bpp, 1);
     p.P = ceil_div(nblk_max, p.bpp);
-    if (p.P <= 1) p = Plan{1, std::max(nblk_max, 1)};
+    if (p.P <= 1) p = Plan{1, std::max(nblk_max, 1), 0, 0, 0};
     return p;
 }
 
+// Stream plan (16-bit and 8-bit caches). Measured on MI355X: the step runs
+// at its best when every compute unit holds the same amount of work, and one
+// workgroup of four streaming waves per compute unit already saturates HBM;
+// so the default is 256 workgroups (1024 wave ranges), fewer when the batch
+// has under 8 blocks per range. The block count T is estimated from the
+// host hints (total_context, else B * max_context); the kernel recomputes the
+// exact split from context_lens, so the estimate only tunes the wave count.
+Plan make_stream_plan(const pda_attn_desc& d) {
+    const int64_t S = (int64_t)d.B * d.n_kv;
+    const int64_t nblk_max = std::min<int64_t>(
+        ceil_div(std::max<int64_t>(d.max_context, 1), d.block_size), d.max_blocks_per_seq);
+    const int64_t t_est = (int64_t)d.n_kv *
+        (d.total_context > 0 ? ceil_div(d.total_context, d.block_size) + d.B : d.B * nblk_max);
+    Plan p{1, (int32_t)std::max<int64_t>(nblk_max, 1), (int32_t)S, 0, 1};
+    if (d.num_partitions == 1) return p;
+    int64_t nw;
+    if (d.num_partitions > 1) {
+        nw = d.num_partitions;
+    } else {
+        const int64_t wgs = std::max(env_int("PDA_ATTN_WORKGROUPS", 256), 1);
+        const int64_t min_blocks = std::max(env_int("PDA_MIN_BLOCKS_PER_WAVE", 8), 1);
+        nw = std::min<int64_t>(4 * wgs, (t_est + min_blocks - 1) / min_blocks);
+        if (nw <= S) return p;   // short contexts: one wave per segment, no merge
+    }
+    nw = std::min<int64_t>(nw, kMaxStreamWaves);
+    p.nw = (int32_t)nw;
+    p.split = 1;
+    p.P = (int32_t)nw;
+    p.bpp = (int32_t)std::max<int64_t>(1, (t_est + nw - 1) / nw);
+    return p;
+}
+
+Plan make_plan(const pda_attn_desc& d) {
+    return d.kv_dtype == PDA_F32 ? make_partition_plan(d) : make_stream_plan(d);
+}
+
 WsLayout ws_layout(const pda_attn_desc& d, const Plan& p) {
-    WsLayout w{0, 0, 0};
+    WsLayout w{0, 0, 0, 0};
+    if (p.stream) {
+        if (!p.split) return w;
+        const size_t S = (size_t)d.B * d.n_kv;
+        const size_t g = (size_t)(d.n_q / d.n_kv);
+        const size_t slots = S + (size_t)p.nw;
+        w.part_o_off = 0;
+        w.part_ml_off = align256(slots * g * d.d_h * sizeof(float));
+        w.seg_info_off = w.part_ml_off + align256(slots * g * 2 * sizeof(float));
+        w.bytes = w.seg_info_off + align256(S * 2 * sizeof(int32_t));
+        return w;
+    }
     if (p.P <= 1) return w;
     const size_t rows = (size_t)d.B * d.n_q;
     w.part_o_off = 0;
@@ -137,6 +180,14 @@ int32_t check_attn_desc(const pda_attn_desc* d, bool quant) {
     if ((d->q_dtype != PDA_F32 && d->q_dtype != PDA_BF16) ||
         (d->out_dtype != PDA_F32 && d->out_dtype != PDA_BF16)) {
         set_error("q_dtype / out_dtype must be F32 or BF16");
+        return PDA_EINVAL;
+    }
+    if (d->kv_dtype != PDA_F32 &&
+        (d->B > kMaxStreamBatch ||
+         (int64_t)d->B * d->n_kv * d->max_blocks_per_seq >= ((int64_t)1 << 31) ||
+         (int64_t)d->B * d->n_kv >= ((int64_t)1 << 24))) {
+        set_error("batch too large for one call: B <= %d and B * n_kv * max_blocks_per_seq < 2^31",
+                  kMaxStreamBatch);
         return PDA_EINVAL;
     }
     if ((int64_t)d->B * d->max_blocks_per_seq > INT32_MAX ||
@@ -228,9 +279,22 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     a.kv_dtype = d->kv_dtype;
     a.q_dtype = d->q_dtype;
     a.out_dtype = d->out_dtype;
+    a.seg_info = ws.bytes ? (int2*)((char*)workspace + ws.seg_info_off) : nullptr;
     a.P = plan.P;
     a.bpp = plan.bpp;
-    hipError_t e = d->kv_dtype == PDA_F32 ? launch_attn_f32(a, s) : launch_attn_mfma(a, s);
+    a.nw = plan.nw;
+    a.split = plan.split;
+    hipError_t e;
+    if (plan.stream) {
+        e = launch_attn_mfma(a, s);
+        if (e != hipSuccess) return hip_fail("attention launch", e);
+        if (plan.split) {
+            e = launch_merge_stream(a, s);
+            if (e != hipSuccess) return hip_fail("merge launch", e);
+        }
+        return PDA_OK;
+    }
+    e = launch_attn_f32(a, s);
     if (e != hipSuccess) return hip_fail("attention launch", e);
     if (plan.P > 1) {
         e = launch_merge_for_attn(a, s);

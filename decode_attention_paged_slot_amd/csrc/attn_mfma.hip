@@ -8,13 +8,21 @@
 // each (block, head) K/V tile serves all g query heads (the GQA reuse that
 // gives 2 g / w_kv FLOP per byte), scores never leave registers.
 //
-// Work decomposition (one workgroup = 4 waves = 256 lanes):
-//   grid = (P partitions, n_kv, B). Partition p of row b owns the contiguous
-//   logical blocks [p * bpp, (p + 1) * bpp) (the last partition runs to the end
-//   of the row); wave w of the workgroup takes blocks w, w + 4, w + 8, ... of
-//   it, each wave with its own online-softmax state; the four states are
-//   merged through LDS at the end. With P > 1 the workgroup writes a partial
-//   (normalised output, max, sum) and a log-sum-exp merge kernel finishes.
+// Work decomposition. A segment is one (sequence b, KV head j) pair with
+// nblk_b = ceil(n_b / 16) blocks; segments are laid end to end (b major, j
+// minor) on one flattened axis of T = n_kv * sum_b nblk_b blocks.
+//  - Split mode: the axis is cut into NW equal contiguous ranges (NW capped
+//    at T), one per wave (four independent waves per workgroup, about one
+//    workgroup per compute unit), so every wave streams the same number of
+//    blocks however ragged the batch is. A wave's range covers pieces of one or more
+//    segments; its load pipeline runs across segment boundaries. A piece
+//    that is a whole segment is normalised and written to the output; any
+//    other piece writes a partial (normalised output, base-2 max, sum) to
+//    slot segment + wave, and the merge kernel combines the pieces of each
+//    split segment, whose wave range [first, last] the wave that starts the
+//    segment records. Each workgroup first computes the per-sequence block
+//    prefix sums from context_lens in LDS (no host round trip).
+//  - Unsplit mode: wave w streams segment w alone and writes its output.
 //
 // Per 16-token block and wave:
 //   S^T[16 tok][16 heads] = K_tile[16][d_h] . Q^T[d_h][16]  -- MFMA 16x16x32 bf16;
@@ -32,7 +40,8 @@
 //     split the same way.
 //   8-bit caches are converted to bf16 in registers (exact), the K scale is
 //   folded into the score multiplier and the V scale into P.
-// Loads run `kDepth` blocks ahead of the math in each wave.
+// Loads run `kDepth` blocks ahead of the math in each wave and are marked
+// non-temporal (every cache byte is read once per step).
 #include "device_common.h"
 #include "pda_internal.h"
 
@@ -98,50 +107,160 @@ __device__ __forceinline__ bf16x8 kv_operand_from_bytes(uint4 w, int half) {
     }
 }
 
+
+// Per-block metadata, lane i of a 64-block batch describing block i.
+//   info bits 0-4 valid tokens (1..16), bit 5 first block of its segment,
+//   bit 6 last block of its segment, bits 7.. segment index.
+struct Meta {
+    int id;      // physical block, or -1 when the table entry is unmapped
+    int info;
+    float ksc, vsc;
+};
+
 template <int HD, int KV, int QT>
-__global__ void __launch_bounds__(kAttnThreads, 2) k_attn_mfma(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     using T = Tr<HD, KV>;
     constexpr bool QUANT = KV != DT_BF16;
-    constexpr int OROW = HD + 4;   // padded fp32 row of the combine buffer
-    constexpr int STAGE_BYTES = 4 * T::LTILE;
-    constexpr int COMB_BYTES = 4 * 16 * OROW * 4 + 4 * 16 * 2 * 4;
-    constexpr int SMEM = STAGE_BYTES > COMB_BYTES ? STAGE_BYTES : COMB_BYTES;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ __attribute__((aligned(16))) char stage_all[4 * T::LTILE];
+    __shared__ int wsum[4];
+    extern __shared__ int dyn_lds[];
+    int* pre = dyn_lds;             // [B + 1] exclusive prefix of blocks per sequence
+    int* nn = dyn_lds + a.B + 1;    // [B] context length, -1 for an invalid one
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int col = lane & 15;   // token row (A operand) / query head (B, D)
     const int grp = lane >> 4;
-    const int b = blockIdx.z, j = blockIdx.y, p = blockIdx.x;
     const int g = a.g;
+    const int B = a.B;
+    const int n_kv = a.n_kv;
 
-    const int n = a.context_lens[b];
-    const bool row_bad = n < 0 || n > a.max_blocks * 16;
-    const int nblk = row_bad ? 0 : (n + 15) >> 4;
-    const int blk0 = p * a.bpp;
-    if (row_bad || blk0 >= nblk) {
-        // unsplit: this workgroup owns the row's output (NaN for a bad row,
-        // zeros for an empty one); split: the merge kernel handles the row
-        if (a.P == 1) {
-            const float v = row_bad ? __builtin_nanf("") : 0.0f;
-            for (int idx = threadIdx.x; idx < g * HD; idx += kAttnThreads) {
-                const int h = idx / HD, d = idx % HD;
-                const int64_t o = ((int64_t)b * a.n_q + j * g + h) * HD + d;
-                if (a.out_dtype == DT_F32) ((float*)a.out)[o] = v;
-                else ((uint16_t*)a.out)[o] = (uint16_t)f32_to_bf16_rne(v);
+    // ---- per-sequence block counts and their exclusive prefix (LDS)
+    {
+        const int R = (B + kAttnThreads - 1) / kAttnThreads;
+        const int r0 = threadIdx.x * R;
+        int local = 0;
+        for (int r = 0; r < R; ++r) {
+            const int b = r0 + r;
+            if (b < B) {
+                const int n = a.context_lens[b];
+                const bool bad = n < 0 || n > a.max_blocks * 16;
+                nn[b] = bad ? -1 : n;
+                local += bad ? 0 : (n + 15) >> 4;
             }
         }
-        return;
+        int incl = local;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int run = incl - local;
+        for (int w = 0; w < wave; ++w) run += wsum[w];
+        for (int r = 0; r < R; ++r) {
+            const int b = r0 + r;
+            if (b < B) {
+                pre[b] = run;
+                run += nn[b] < 0 ? 0 : (nn[b] + 15) >> 4;
+            }
+        }
+        if (threadIdx.x == kAttnThreads - 1) pre[B] = run;
+        __syncthreads();
     }
-    const int blk1 = (p == a.P - 1) ? nblk : min(nblk, blk0 + a.bpp);
-    const int nb_wg = blk1 - blk0;
-    const int my_cnt = nb_wg > wave ? (nb_wg - wave + 3) >> 2 : 0;
+    const int64_t T_all = (int64_t)n_kv * pre[B];
+    // never more ranges than blocks: every range in use is non-empty, so the
+    // pieces of a segment come from consecutive waves without gaps
+    const int NW = (int)max((int64_t)1, min((int64_t)a.nw, T_all));
+    const int wg = blockIdx.x * 4 + wave;   // global wave index
 
-    // ---- query operands (B operand of S^T = K . Q^T): lane (h, grp)
+    // ---- this wave's range [lo, hi) of the flattened axis
+    int64_t lo = 0, hi = 0;
+    if (a.split) {
+        if (wg < NW) {
+            lo = (int64_t)wg * T_all / NW;
+            hi = (int64_t)(wg + 1) * T_all / NW;
+        }
+    } else if (wg < B * n_kv) {
+        const int b = wg / n_kv, j = wg - (wg / n_kv) * n_kv;
+        const int nb = pre[b + 1] - pre[b];
+        lo = (int64_t)n_kv * pre[b] + (int64_t)j * nb;
+        hi = lo + nb;
+    }
+
+    auto write_rows = [&](int64_t row0, int nrows, float v) {
+        for (int idx = lane; idx < nrows * HD; idx += 64) {
+            const int64_t o = row0 * HD + idx;
+            if (a.out_dtype == DT_F32) ((float*)a.out)[o] = v;
+            else ((uint16_t*)a.out)[o] = (uint16_t)f32_to_bf16_rne(v);
+        }
+    };
+
+    // ---- sequences without blocks (empty, or invalid length): zero / NaN rows.
+    // Split mode: such a sequence sits at position n_kv * pre[b]; the wave
+    // whose range holds that position owns it (the last wave also owns the
+    // position T_all). Unsplit mode: the wave of each of its segments.
+    if (a.split) {
+        if (wg < NW) {
+            const int64_t hi_ext = (wg == NW - 1) ? T_all + 1 : hi;
+            int l = 0, r = B;
+            while (l < r) {
+                const int mid = (l + r) >> 1;
+                if ((int64_t)n_kv * pre[mid] >= lo) r = mid;
+                else l = mid + 1;
+            }
+            for (int b = l; b < B && (int64_t)n_kv * pre[b] < hi_ext; ++b) {
+                if (pre[b + 1] != pre[b]) continue;
+                write_rows((int64_t)b * a.n_q, a.n_q, nn[b] < 0 ? __builtin_nanf("") : 0.0f);
+                for (int jj = lane; jj < n_kv; jj += 64)
+                    a.seg_info[(int64_t)b * n_kv + jj] = make_int2(0, -1);
+            }
+        }
+    } else if (wg < B * n_kv && hi == lo) {
+        write_rows((int64_t)wg * g, g, nn[wg / n_kv] < 0 ? __builtin_nanf("") : 0.0f);
+    }
+
+    const int cnt = (int)(hi - lo);
+    if (cnt <= 0) return;
+
+    // ---- per-block metadata of batch `batch` (64 blocks from lo + 64 * batch)
+    auto load_meta = [&](int batch) {
+        Meta m{-1, 0, 1.0f, 1.0f};
+        const int64_t f = lo + (int64_t)batch * 64 + lane;
+        if (f < hi) {
+            const int x = (int)f;
+            int l = 0, r = B - 1;   // last sequence whose first position is <= x
+            while (l < r) {
+                const int mid = (l + r + 1) >> 1;
+                if (n_kv * pre[mid] <= x) l = mid;
+                else r = mid - 1;
+            }
+            const int b = l;
+            const int nb = pre[b + 1] - pre[b];
+            const int r0 = x - n_kv * pre[b];
+            const int j = r0 / nb;
+            const int blk = r0 - j * nb;
+            int id = a.block_table[(int64_t)b * a.max_blocks + blk];
+            if (id < 0 || id >= a.num_blocks) id = -1;
+            const int valid = min(16, nn[b] - 16 * blk);
+            const int seg = b * n_kv + j;
+            m.id = id;
+            m.info = valid | ((blk == 0) << 5) | ((blk == nb - 1) << 6) | (seg << 7);
+            if (QUANT && id >= 0) {
+                m.ksc = a.k_scale[(int64_t)id * n_kv + j];
+                m.vsc = a.v_scale[(int64_t)id * n_kv + j];
+            }
+        }
+        return m;
+    };
+
+    // ---- query operands (B operand of S^T = K . Q^T): lane (h, grp), for
+    // the g query rows of segment `seg` (rows seg * g .. seg * g + g - 1)
     bf16x8 qhi[T::NCH], qlo[T::NCH];
-    {
+    auto load_q = [&](int seg) {
         const bool live = col < g;
-        const int64_t qrow = ((int64_t)b * a.n_q + j * g + (live ? col : 0)) * HD;
+        const int64_t qrow = ((int64_t)seg * g + (live ? col : 0)) * HD;
 #pragma unroll
         for (int c = 0; c < T::NCH; ++c) {
             const int d0 = dmap<HD, KV>(c, grp);
@@ -168,21 +287,23 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_attn_mfma(AttnArgs a) {
                 qlo[c] = __builtin_bit_cast(bf16x8, lv);
             }
         }
-    }
+    };
 
-    // ---- per-wave state
+    // ---- per-piece online-softmax state
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
     f32x4 acc[T::NT];
 #pragma unroll
     for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-    bool bad = false;
+    bool piece_bad = false;
+    bool piece_whole = false;   // the current piece began at its segment's first block
+    int q_seg = -1;
 
-    char* stage = smem + wave * T::LTILE;
+    char* stage = stage_all + wave * T::LTILE;
     const char* kbase = (const char*)a.k;
     const char* vbase = (const char*)a.v;
     const int64_t head_stride = T::TILEB;
-    const int64_t block_stride = (int64_t)a.n_kv * T::TILEB;
+    const int64_t block_stride = (int64_t)n_kv * T::TILEB;
 
     // V row / chunk handled by this lane for load l of a tile
     int vrow[T::LOADS], vcb[T::LOADS];
@@ -201,198 +322,218 @@ __global__ void __launch_bounds__(kAttnThreads, 2) k_attn_mfma(AttnArgs a) {
         trd[t] = lds_off<HD>(r, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
     }
 
-    for (int base = 0; base < my_cnt && !bad; base += 64) {
-        const int cnt = min(64, my_cnt - base);
-        // lane i holds the physical block (and scales) of this wave's i-th block
-        int id = 0;
-        float ksc = 1.0f, vsc = 1.0f;
-        const int kb_lane = blk0 + wave + 4 * (base + lane);
-        if (lane < cnt) {
-            id = a.block_table[(int64_t)b * a.max_blocks + kb_lane];
-            if (QUANT && id >= 0 && id < a.num_blocks) {
-                ksc = a.k_scale[(int64_t)id * a.n_kv + j];
-                vsc = a.v_scale[(int64_t)id * a.n_kv + j];
-            }
-        }
-        if (__ballot(lane < cnt && (id < 0 || id >= a.num_blocks)) != 0) {
-            bad = true;
-            break;
-        }
+    // metadata of the consumer's batch (A) and of the next one (Bm)
+    Meta A = load_meta(0);
+    Meta Bm = cnt > 64 ? load_meta(1) : Meta{-1, 0, 1.0f, 1.0f};
+    int batchA = 0;
+    auto meta_id = [&](int i) {
+        const int v = (i >> 6) == batchA ? A.id : Bm.id;
+        return __builtin_amdgcn_readlane(v, i & 63);
+    };
+    auto meta_info = [&](int i) {
+        const int v = (i >> 6) == batchA ? A.info : Bm.info;
+        return __builtin_amdgcn_readlane(v, i & 63);
+    };
+    auto meta_f = [&](float fa, float fb, int i) {
+        const float v = (i >> 6) == batchA ? fa : fb;
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i & 63));
+    };
 
-        uint4 kr[kDepth][T::LOADS], vr[kDepth][T::LOADS];
+    uint4 kr[kDepth][T::LOADS], vr[kDepth][T::LOADS];
 
-        // Loads are never predicated (a partially filled final block is still a
-        // whole allocated tile; its tail rows are masked after loading), so
-        // every refill issues the same instructions and the waits before each
-        // block's math only drain that block's loads.
-        auto issue = [&](int s, int i) {
-            const int pb = __builtin_amdgcn_readlane(id, i);
-            const char* kt = kbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
-            const char* vt = vbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
+    // Loads are never predicated (a partially filled final block is still a
+    // whole allocated tile; its tail rows are masked after loading; an
+    // unmapped entry loads block 0 and poisons its piece), so every refill
+    // issues the same instructions and the waits before each block's math
+    // only drain that block's loads.
+    auto issue = [&](int s, int i) {
+        int pb = meta_id(i);
+        pb = pb < 0 ? 0 : pb;
+        const int j = (int)((unsigned)meta_info(i) >> 7) % n_kv;
+        const char* kt = kbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
+        const char* vt = vbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16_stream(kt + col * T::ROWB + 64 * l + 16 * grp);
+        for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16_stream(kt + col * T::ROWB + 64 * l + 16 * grp);
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l) vr[s][l] = ld16_stream(vt + 1024 * l + 16 * lane);
-        };
+        for (int l = 0; l < T::LOADS; ++l) vr[s][l] = ld16_stream(vt + 1024 * l + 16 * lane);
+    };
 
-        auto consume = [&](int s, int i, bool refill) {
-            const int kb = blk0 + wave + 4 * (base + i);
-            const int valid = min(16, n - 16 * kb);
-            if (valid < 16) {
-                // rows past the row's end hold stale data (possibly NaN):
-                // zero them so that 0-weight products stay 0
+    auto flush = [&](int seg, bool whole) {
+        float l_tot = l_run + fshfl_xor(l_run, 16);
+        l_tot += fshfl_xor(l_tot, 32);
+        if (piece_bad) l_tot = __builtin_nanf("");
+        if (col < g) {
+            const int64_t prow = whole ? (int64_t)seg * g + col : ((int64_t)seg + wg) * g + col;
+            f32x4 r[T::NT];
 #pragma unroll
-                for (int l = 0; l < T::LOADS; ++l)
-                    if (vrow[l] >= valid) vr[s][l] = make_uint4(0, 0, 0, 0);
-            }
-            // stage V (as bf16) into this wave's LDS tile
+            for (int t = 0; t < T::NT; ++t)
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l) {
-                if (KV == DT_BF16) {
-                    *(uint4*)(stage + lds_off<HD>(vrow[l], vcb[l])) = vr[s][l];
-                } else {
-                    const bf16x8 v0 = kv_operand_from_bytes<KV>(vr[s][l], 0);
-                    const bf16x8 v1 = kv_operand_from_bytes<KV>(vr[s][l], 1);
-                    *(bf16x8*)(stage + lds_off<HD>(vrow[l], vcb[l])) = v0;
-                    *(bf16x8*)(stage + lds_off<HD>(vrow[l], vcb[l] + 1)) = v1;
+                for (int e = 0; e < 4; ++e) r[t][e] = l_tot != 0.0f ? acc[t][e] / l_tot : 0.0f;
+            if (!whole) {
+#pragma unroll
+                for (int t = 0; t < T::NT; ++t)
+                    *(f32x4*)(a.part_o + prow * HD + 16 * t + 4 * grp) = r[t];
+                if (grp == 0) *(float2*)(a.part_ml + prow * 2) = make_float2(m_run, l_tot);
+            } else if (a.out_dtype == DT_F32) {
+#pragma unroll
+                for (int t = 0; t < T::NT; ++t)
+                    *(f32x4*)((float*)a.out + prow * HD + 16 * t + 4 * grp) = r[t];
+            } else {
+#pragma unroll
+                for (int t = 0; t < T::NT; ++t) {
+                    uint2 h;
+                    h.x = f32_to_bf16_rne(r[t][0]) | (f32_to_bf16_rne(r[t][1]) << 16);
+                    h.y = f32_to_bf16_rne(r[t][2]) | (f32_to_bf16_rne(r[t][3]) << 16);
+                    *(uint2*)((uint16_t*)a.out + prow * HD + 16 * t + 4 * grp) = h;
                 }
             }
-            // scores S^T = K . Q^T
-            f32x4 st = {0, 0, 0, 0};
-#pragma unroll
-            for (int c = 0; c < T::NCH; ++c) {
-                bf16x8 kop;
-                if constexpr (KV == DT_BF16) kop = kv_operand_from_bytes<KV>(kr[s][c], 0);
-                else kop = kv_operand_from_bytes<KV>(kr[s][c / 2], c % 2);
-                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[c], st, 0, 0, 0);
-                if (QT == DT_F32) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
-            }
-            // refill this slot with the block kDepth ahead
-            if (refill) issue(s, i + kDepth);
-
-            // online softmax over this block's 16 tokens (base-2 domain)
-            const float mult = QUANT ? a.scale_log2 * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ksc), i))
-                                     : a.scale_log2;
-            float sv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sv[e] = st[e] * mult;
-                if (valid < 16 && 4 * grp + e >= valid) sv[e] = -__builtin_inff();
-            }
-            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            mx = fmaxf(mx, fshfl_xor(mx, 16));
-            mx = fmaxf(mx, fshfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            float pe[4], psum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
-                psum += pe[e];
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-#pragma unroll
-            for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
-
-            const float vs = QUANT ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vsc), i))
-                                   : 1.0f;
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) split_bf16(pe[e] * vs, hi[e], lo[e]);
-            const s16x4 phi = {(short)hi[0], (short)hi[1], (short)hi[2], (short)hi[3]};
-            const s16x4 plo = {(short)lo[0], (short)lo[1], (short)lo[2], (short)lo[3]};
-
-            // O^T += V^T . P^T
-#pragma unroll
-            for (int t = 0; t < T::NT; ++t) {
-                const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(stage + trd[t]));
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo, acc[t], 0, 0, 0);
-            }
-        };
-
-        int it = 0;
-        if (cnt >= 2 * kDepth) {
-            // prologue and steady state issue unconditionally and in slot
-            // order (the scheduling barriers keep the prologue's independent
-            // loads from being reordered), so at the loop head the newest loads
-            // are always the other slots' and each block waits only for itself
-#pragma unroll
-            for (int s = 0; s < kDepth; ++s) {
-                issue(s, s);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            for (; it + 2 * kDepth <= cnt; it += kDepth) {
-#pragma unroll
-                for (int s = 0; s < kDepth; ++s) consume(s, it + s, true);
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < kDepth; ++s)
-                if (s < cnt) issue(s, s);
         }
-        // drain: fewer than 2 * kDepth blocks remain, their first loads issued
+        m_run = -__builtin_inff();
+        l_run = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 2 * kDepth; ++k)
-            if (it + k < cnt) consume(k % kDepth, it + k, it + k + kDepth < cnt);
+        for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+        piece_bad = false;
+    };
+
+    auto consume = [&](int s, int i, bool refill) {
+        if ((i >> 6) != batchA) {   // the consumer enters the next batch
+            A = Bm;
+            ++batchA;
+            if ((batchA + 1) * 64 < cnt) Bm = load_meta(batchA + 1);
+        }
+        const int info = meta_info(i);
+        const int valid = info & 31;
+        const bool seg_first = (info >> 5) & 1;
+        const bool seg_last = (info >> 6) & 1;
+        const int seg = (int)((unsigned)info >> 7);
+        if (seg_first || i == 0) {   // a new piece starts here
+            piece_whole = seg_first;
+            if (seg != q_seg) {
+                load_q(seg);
+                q_seg = seg;
+            }
+            if (a.split && seg_first && lane == 0) {
+                // record the waves covering this segment for the merge
+                const int b = seg / n_kv;
+                const int64_t end = lo + i + (pre[b + 1] - pre[b]);
+                const int last_wave = (int)((end * NW - 1) / T_all);
+                a.seg_info[seg] = make_int2(wg, last_wave);
+            }
+        }
+        if (meta_id(i) < 0) piece_bad = true;
+        if (valid < 16) {
+            // rows past the sequence's end hold stale data (possibly NaN):
+            // zero them so that 0-weight products stay 0
+#pragma unroll
+            for (int l = 0; l < T::LOADS; ++l)
+                if (vrow[l] >= valid) vr[s][l] = make_uint4(0, 0, 0, 0);
+        }
+        // stage V (as bf16) into this wave's LDS tile
+#pragma unroll
+        for (int l = 0; l < T::LOADS; ++l) {
+            if (KV == DT_BF16) {
+                *(uint4*)(stage + lds_off<HD>(vrow[l], vcb[l])) = vr[s][l];
+            } else {
+                const bf16x8 v0 = kv_operand_from_bytes<KV>(vr[s][l], 0);
+                const bf16x8 v1 = kv_operand_from_bytes<KV>(vr[s][l], 1);
+                *(bf16x8*)(stage + lds_off<HD>(vrow[l], vcb[l])) = v0;
+                *(bf16x8*)(stage + lds_off<HD>(vrow[l], vcb[l] + 1)) = v1;
+            }
+        }
+        // scores S^T = K . Q^T
+        f32x4 st = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < T::NCH; ++c) {
+            bf16x8 kop;
+            if constexpr (KV == DT_BF16) kop = kv_operand_from_bytes<KV>(kr[s][c], 0);
+            else kop = kv_operand_from_bytes<KV>(kr[s][c / 2], c % 2);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[c], st, 0, 0, 0);
+            if (QT == DT_F32) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
+        }
+        const float ksc = QUANT ? meta_f(A.ksc, Bm.ksc, i) : 1.0f;
+        const float vsc = QUANT ? meta_f(A.vsc, Bm.vsc, i) : 1.0f;
+        // refill this slot with the block kDepth ahead
+        if (refill) issue(s, i + kDepth);
+
+        // online softmax over this block's 16 tokens (base-2 domain)
+        const float mult = a.scale_log2 * ksc;
+        float sv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = st[e] * mult;
+            if (valid < 16 && 4 * grp + e >= valid) sv[e] = -__builtin_inff();
+        }
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, fshfl_xor(mx, 16));
+        mx = fmaxf(mx, fshfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float pe[4], psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+            psum += pe[e];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
+
+        uint32_t hi16[4], lo16[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(pe[e] * vsc, hi16[e], lo16[e]);
+        const s16x4 phi = {(short)hi16[0], (short)hi16[1], (short)hi16[2], (short)hi16[3]};
+        const s16x4 plo = {(short)lo16[0], (short)lo16[1], (short)lo16[2], (short)lo16[3]};
+
+        // O^T += V^T . P^T
+#pragma unroll
+        for (int t = 0; t < T::NT; ++t) {
+            const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(stage + trd[t]));
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo, acc[t], 0, 0, 0);
+        }
+        if (seg_last || i == cnt - 1) flush(seg, piece_whole && seg_last);
+    };
+
+    int it = 0;
+    if (cnt >= 2 * kDepth) {
+        // prologue and steady state issue unconditionally and in slot order
+        // (the scheduling barriers keep the prologue's independent loads from
+        // being reordered), so at the loop head the newest loads are always
+        // the other slots' and each block waits only for itself
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) {
+            issue(s, s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (; it + 2 * kDepth <= cnt; it += kDepth) {
+#pragma unroll
+            for (int s = 0; s < kDepth; ++s) consume(s, it + s, true);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s)
+            if (s < cnt) issue(s, s);
     }
-
-    // ---- merge the four waves' states through LDS
-    float l_tot = l_run + fshfl_xor(l_run, 16);
-    l_tot += fshfl_xor(l_tot, 32);
-    if (bad) l_tot = __builtin_nanf("");
-    __syncthreads();   // staging area is reused below
-    float* lo_buf = (float*)smem;                        // [4][16][OROW]
-    float* ml_buf = (float*)(smem + 4 * 16 * OROW * 4);  // [4][16][2]
-    if (col < g) {
+    // drain: fewer than 2 * kDepth blocks remain, their first loads issued
 #pragma unroll
-        for (int t = 0; t < T::NT; ++t)
-            *(f32x4*)(lo_buf + (wave * 16 + col) * OROW + 16 * t + 4 * grp) = acc[t];
-        if (grp == 0) {
-            ml_buf[(wave * 16 + col) * 2 + 0] = m_run;
-            ml_buf[(wave * 16 + col) * 2 + 1] = l_tot;
-        }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < g * HD; idx += kAttnThreads) {
-        const int h = idx / HD, d = idx % HD;
-        float M = -__builtin_inff();
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_buf[(w * 16 + h) * 2]);
-        float L = 0.0f, o = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float mw = ml_buf[(w * 16 + h) * 2];
-            const float sc = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-            L += sc * ml_buf[(w * 16 + h) * 2 + 1];
-            o += sc * lo_buf[(w * 16 + h) * OROW + d];
-        }
-        const int64_t row = (int64_t)b * a.n_q + j * g + h;
-        const float r = L != 0.0f ? o / L : 0.0f;
-        if (a.P > 1) {
-            a.part_o[(row * a.P + p) * HD + d] = r;
-            if (d == 0) {
-                a.part_ml[(row * a.P + p) * 2 + 0] = M;
-                a.part_ml[(row * a.P + p) * 2 + 1] = L;
-            }
-        } else if (a.out_dtype == DT_F32) {
-            ((float*)a.out)[row * HD + d] = r;
-        } else {
-            ((uint16_t*)a.out)[row * HD + d] = (uint16_t)f32_to_bf16_rne(r);
-        }
-    }
+    for (int k = 0; k < 2 * kDepth; ++k)
+        if (it + k < cnt) consume(k % kDepth, it + k, it + k + kDepth < cnt);
 }
 
 }  // namespace
 
+size_t attn_mfma_dyn_lds(int32_t B) { return (size_t)(2 * B + 1) * sizeof(int32_t); }
+
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-    dim3 grid(a.P, a.n_kv, a.B);
+    const int waves = a.split ? a.nw : a.B * a.n_kv;
+    dim3 grid((waves + 3) / 4);
     dim3 block(kAttnThreads);
+    const size_t lds = attn_mfma_dyn_lds(a.B);
 #define PDA_LAUNCH(HD, KV, QT) \
-    hipLaunchKernelGGL((k_attn_mfma<HD, KV, QT>), grid, block, 0, s, a)
+    hipLaunchKernelGGL((k_attn_mfma<HD, KV, QT>), grid, block, lds, s, a)
 #define PDA_BY_Q(HD, KV)                          \
     if (a.q_dtype == DT_BF16) PDA_LAUNCH(HD, KV, DT_BF16); \
     else PDA_LAUNCH(HD, KV, DT_F32)

@@ -39,16 +39,70 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return v;
 }
 
-// context_lens != nullptr: row r belongs to sequence r / n_q and uses the
-// partitions its length needs (ceil(ceil(n / 16) / bpp), capped at P);
-// otherwise all P partials are read and l_p == 0 marks an empty one.
-//
-// Phase 1: every thread takes partitions p = tid, tid + 256, ... for the
-// block-wide max M and the weights w_p = l_p 2^(m_p - M), kept in LDS.
-// Phase 2: thread (sub, c) accumulates the 4-float column group c of the
+// Merge of np partials of one output row into `out_row` (HD floats or
+// bf16): partial p has statistics (m, l) at ml + p * sm and output at
+// po + p * so. Phase 1: every thread takes partials p = tid, tid + 256, ...
+// for the block-wide max M and the weights w_p = l_p 2^(m_p - M), kept in
+// LDS. Phase 2: thread (sub, c) accumulates the 4-float column group c of the
 // partials p = sub, sub + SUB, ... (loads are unconditional, so they can all
 // be in flight together; an empty partial's weight is 0 and its data unused);
 // the SUB partial sums are added through LDS.
+template <int HD>
+__device__ __forceinline__ void merge_row(const float* __restrict__ po, int64_t so,
+                                          const float* __restrict__ ml, int64_t sm, int np,
+                                          bool row_bad, void* out_row, int32_t out_dtype,
+                                          float* wsh, float* red, f32x4* acc_sh) {
+    constexpr int V = HD / 4;          // float4 column groups per row
+    constexpr int SUB = kThreads / V;  // partial subsets
+    float mloc = -__builtin_inff();
+    for (int p = threadIdx.x; p < np; p += kThreads) {
+        const float2 x = *(const float2*)(ml + p * sm);
+        if (x.y != 0.0f) mloc = fmaxf(mloc, x.x);
+    }
+    const float M = block_max(mloc, red);
+    float lsum = 0.0f;
+    for (int p = threadIdx.x; p < np; p += kThreads) {
+        const float2 x = *(const float2*)(ml + p * sm);
+        const float w = x.y == 0.0f ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
+        wsh[p] = w;
+        lsum += w;
+    }
+    const float L = block_sum(lsum, red);   // its barriers also publish wsh
+    const int c = threadIdx.x % V, sub = threadIdx.x / V;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int p = sub; p < np; p += SUB) {
+        const f32x4 o = *((const f32x4*)(po + p * so) + c);
+        const float w = wsh[p];
+        if (w != 0.0f) acc += w * o;
+    }
+    acc_sh[sub * V + c] = acc;
+    __syncthreads();
+    if (sub == 0) {
+        f32x4 tot = acc_sh[c];
+#pragma unroll
+        for (int k = 1; k < SUB; ++k) tot += acc_sh[k * V + c];
+        f32x4 r;
+        const bool ok = L != 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = ok ? tot[e] / L : 0.0f;
+        if (row_bad) r = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                               __builtin_nanf("")};
+        if (out_dtype == DT_F32) {
+            *((f32x4*)out_row + c) = r;
+        } else {
+            uint2 h;
+            h.x = f32_to_bf16_rne(r[0]) | (f32_to_bf16_rne(r[1]) << 16);
+            h.y = f32_to_bf16_rne(r[2]) | (f32_to_bf16_rne(r[3]) << 16);
+            *((uint2*)out_row + c) = h;
+        }
+    }
+}
+
+// Partition layout (rows x P partials). context_lens != nullptr: row r
+// belongs to sequence r / n_q and uses the partitions its length needs
+// (ceil(ceil(n / 16) / bpp), capped at P); otherwise all P partials are read
+// and l_p == 0 marks an empty one.
 template <int HD>
 __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -56,11 +110,9 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
                                                     int32_t n_q, int32_t P, int32_t bpp,
                                                     int32_t max_blocks, void* out,
                                                     int32_t out_dtype) {
-    constexpr int V = HD / 4;          // float4 column groups per row
-    constexpr int SUB = kThreads / V;  // partition subsets
     __shared__ float wsh[kMaxPartitions];
     __shared__ float red[4];
-    __shared__ f32x4 acc_sh[SUB][V];
+    __shared__ f32x4 acc_sh[kThreads];
     const int64_t row = blockIdx.x;
     int np = P;
     bool row_bad = false;
@@ -70,51 +122,35 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
         const int nblk = row_bad ? 0 : (n + 15) >> 4;
         np = min(P, (nblk + bpp - 1) / bpp);
     }
-    const float* ml = part_ml + row * (int64_t)P * 2;
-    float mloc = -__builtin_inff();
-    for (int p = threadIdx.x; p < np; p += kThreads) {
-        const float2 x = *(const float2*)(ml + 2 * p);
-        if (x.y != 0.0f) mloc = fmaxf(mloc, x.x);
-    }
-    const float M = block_max(mloc, red);
-    float lsum = 0.0f;
-    for (int p = threadIdx.x; p < np; p += kThreads) {
-        const float2 x = *(const float2*)(ml + 2 * p);
-        const float w = x.y == 0.0f ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
-        wsh[p] = w;
-        lsum += w;
-    }
-    const float L = block_sum(lsum, red);   // its barriers also publish wsh
-    const int c = threadIdx.x % V, sub = threadIdx.x / V;
-    const f32x4* po = (const f32x4*)(part_o + row * (int64_t)P * HD) + c;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-    for (int p = sub; p < np; p += SUB) {
-        const f32x4 o = po[(int64_t)p * V];
-        const float w = wsh[p];
-        if (w != 0.0f) acc += w * o;
-    }
-    acc_sh[sub][c] = acc;
-    __syncthreads();
-    if (sub == 0) {
-        f32x4 tot = acc_sh[0][c];
-#pragma unroll
-        for (int k = 1; k < SUB; ++k) tot += acc_sh[k][c];
-        f32x4 r;
-        const bool inv_ok = L != 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = inv_ok ? tot[e] / L : 0.0f;
-        if (row_bad) r = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                               __builtin_nanf("")};
-        if (out_dtype == DT_F32) {
-            *((f32x4*)((float*)out + row * HD) + c) = r;
-        } else {
-            uint2 h;
-            h.x = f32_to_bf16_rne(r[0]) | (f32_to_bf16_rne(r[1]) << 16);
-            h.y = f32_to_bf16_rne(r[2]) | (f32_to_bf16_rne(r[3]) << 16);
-            *((uint2*)((uint16_t*)out + row * HD) + c) = h;
-        }
-    }
+    char* orow = (char*)out + row * HD * (out_dtype == DT_F32 ? 4 : 2);
+    merge_row<HD>(part_o + row * (int64_t)P * HD, HD, part_ml + row * (int64_t)P * 2, 2, np,
+                  row_bad, orow, out_dtype, wsh, red, acc_sh);
+}
+
+// Stream layout (attention kernel's split mode): output row r = seg * g + hh
+// of segment seg; the pieces of a split segment sit in slots seg + w for the
+// waves w in seg_info[seg] = (first, last), piece row (seg + w) * g + hh.
+// Segments with a single piece (written by the attention kernel directly)
+// or none (zero / NaN rows, also written there) are skipped.
+template <int HD>
+__global__ void __launch_bounds__(kThreads) k_merge_stream(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           const int2* __restrict__ seg_info,
+                                                           int32_t g, void* out,
+                                                           int32_t out_dtype) {
+    __shared__ float wsh[kMaxStreamWaves];
+    __shared__ float red[4];
+    __shared__ f32x4 acc_sh[kThreads];
+    const int64_t row = blockIdx.x;
+    const int64_t seg = row / g;
+    const int hh = (int)(row - seg * g);
+    const int2 info = seg_info[seg];
+    const int np = info.y - info.x + 1;
+    if (np <= 1) return;
+    const int64_t prow0 = (seg + info.x) * g + hh;
+    char* orow = (char*)out + row * HD * (out_dtype == DT_F32 ? 4 : 2);
+    merge_row<HD>(part_o + prow0 * HD, (int64_t)g * HD, part_ml + prow0 * 2, (int64_t)g * 2,
+                  np, false, orow, out_dtype, wsh, red, acc_sh);
 }
 
 hipError_t launch_merge(const float* part_o, const float* part_ml, const int32_t* context_lens,
@@ -135,6 +171,18 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, const int32_t
 hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s) {
     return launch_merge(a.part_o, a.part_ml, a.context_lens, a.B * a.n_q, a.n_q, a.P, a.bpp,
                         a.max_blocks, a.d_h, a.out, a.out_dtype, s);
+}
+
+hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s) {
+    const int64_t rows = (int64_t)a.B * a.n_q;
+    if (rows == 0) return hipSuccess;
+    if (a.d_h == 128)
+        hipLaunchKernelGGL((k_merge_stream<128>), dim3(rows), dim3(kThreads), 0, s, a.part_o,
+                           a.part_ml, a.seg_info, a.g, a.out, a.out_dtype);
+    else
+        hipLaunchKernelGGL((k_merge_stream<64>), dim3(rows), dim3(kThreads), 0, s, a.part_o,
+                           a.part_ml, a.seg_info, a.g, a.out, a.out_dtype);
+    return hipGetLastError();
 }
 
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,

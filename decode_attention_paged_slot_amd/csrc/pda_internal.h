@@ -10,16 +10,25 @@ namespace pda {
 
 void set_error(const char* fmt, ...);
 
-// Split-KV plan: P partitions of `bpp` logical blocks each.
+// Split plan.
+//  fp32 caches (partition plan): P partitions of `bpp` logical blocks per
+//    sequence, grid (P, n_q, B).
+//  16-bit and 8-bit caches (stream plan): split = 1 cuts the flattened
+//    (sequence, KV head, block) axis into `nw` equal wave ranges; split = 0
+//    gives one wave per (sequence, KV head). P reports nw when split, else 1;
+//    bpp the expected blocks per range.
 struct Plan {
     int32_t P;
     int32_t bpp;
+    int32_t nw;
+    int32_t split;
+    int32_t stream;
 };
 Plan make_plan(const pda_attn_desc& d);
 
 // Workspace layout for a plan.
 struct WsLayout {
-    size_t part_o_off, part_ml_off, bytes;
+    size_t part_o_off, part_ml_off, seg_info_off, bytes;
 };
 WsLayout ws_layout(const pda_attn_desc& d, const Plan& p);
 
@@ -46,20 +55,26 @@ struct AttnArgs {
     const int32_t* block_table;
     const int32_t* context_lens;
     void* out;
-    float* part_o;   // [B][n_q][P][d_h]  (split runs only)
-    float* part_ml;  // [B][n_q][P][2]
+    float* part_o;   // partition plan: [B][n_q][P][d_h]; stream plan: [S + nw][g][d_h]
+    float* part_ml;  // partition plan: [B][n_q][P][2];   stream plan: [S + nw][g][2]
+    int2* seg_info;  // stream plan: [S] (first wave, last wave) of each segment
     float scale_log2;  // softmax scale * log2(e)
     int32_t B, n_q, n_kv, g, d_h, max_blocks, num_blocks;
     int32_t kv_dtype, q_dtype, out_dtype;
     int32_t P, bpp;
+    int32_t nw, split;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s);
+size_t attn_mfma_dyn_lds(int32_t B);
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,
                             int32_t d_h, float* out, hipStream_t s);
 
 constexpr int kBlockSize = 16;
 constexpr int kMaxPartitions = 2048;
+constexpr int kMaxStreamBatch = 4096;      // sequences per call on the stream plan (LDS prefix)
+constexpr int kMaxStreamWaves = 8192;      // wave ranges on the stream plan (merge LDS)
 constexpr int kAttnThreads = 256;
 
 }  // namespace pda

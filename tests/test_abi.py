@@ -64,20 +64,42 @@ def test_attention_descriptor_validation(bad):
 
 
 def test_workspace_and_plan():
+    # 16-bit cache (stream plan): 1 = one wave per (sequence, KV head), no workspace
     d = _desc(num_partitions=1)
     assert pda.attn_workspace_size(d) == 0
-    assert pda.attn_plan(d) == (1, 63)
+    assert pda.attn_plan(d)[0] == 1
+    # k > 1: k equal wave ranges over the flattened (sequence, head, block) axis;
+    # workspace = partials of (segments + k) slots x g rows, then segment info
     d = _desc(num_partitions=4)
     P, bpp = pda.attn_plan(d)
-    assert (P, bpp) == (4, 16)
+    assert P == 4 and bpp >= 1
+    g, S = 4, 2 * 2
     ws = pda.attn_workspace_size(d)
-    assert ws >= 2 * 8 * 4 * (128 + 2) * 4
-    # 70B layer shape: B=8, n_kv=8, 32k context -> split with <= 2048 partitions
+    assert ws >= (S + 4) * g * (128 + 2) * 4 + S * 8
+    # 70B layer shape: B=8, n_kv=8, 32k context -> 1024 wave ranges (256 workgroups)
     d = _desc(B=8, n_q=64, n_kv=8, max_blocks_per_seq=2048, num_blocks=18205,
               max_context=32768, total_context=8 * 32768)
     P, bpp = pda.attn_plan(d)
-    assert P * bpp >= 2048 and 1 < P <= 2048 and bpp % 4 == 0
-    assert pda.attn_workspace_size(d) < 0.02 * 8 * 8 * 32768 * 512
+    assert P == 1024 and 128 <= bpp <= 129
+    assert pda.attn_workspace_size(d) < 0.01 * 8 * 8 * 32768 * 512
+    # a batch of short contexts is not split (under 8 blocks per range)
+    d = _desc(B=64, n_q=32, n_kv=8, max_blocks_per_seq=4, max_context=40, total_context=64 * 40)
+    assert pda.attn_plan(d)[0] == 1 and pda.attn_workspace_size(d) == 0
+    # fp32 cache (partition plan): P partitions of bpp blocks per sequence
+    d = _desc(kv_dtype=pda.F32, num_partitions=1)
+    assert pda.attn_workspace_size(d) == 0
+    assert pda.attn_plan(d) == (1, 63)
+    d = _desc(kv_dtype=pda.F32, num_partitions=4)
+    assert pda.attn_plan(d) == (4, 16)
+    assert pda.attn_workspace_size(d) >= 2 * 8 * 4 * (128 + 2) * 4
+
+
+def test_stream_plan_limits():
+    # more than 4096 sequences, or a flattened block axis of 2^31, in one call
+    with pytest.raises(pda.PdaError):
+        pda.attn_workspace_size(_desc(B=4097, max_blocks_per_seq=4))
+    with pytest.raises(pda.PdaError):
+        pda.attn_workspace_size(_desc(B=4096, n_q=64, n_kv=64, max_blocks_per_seq=8192))
 
 
 def test_cache_dtype_must_match_the_call():

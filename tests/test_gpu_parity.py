@@ -49,6 +49,38 @@ def test_split_partitions_agree(parts):
     assert max_err(got, ref) < TOL_16BIT
 
 
+@pytest.mark.parametrize("nw", [2, 3, 5, 7, 13, 64, 1000])
+@pytest.mark.parametrize("kv_dtype", [BF16, FP8])
+def test_stream_ranges_ragged_with_empty_rows(nw, kv_dtype):
+    """Wave ranges cut the flattened (sequence, KV head, block) axis at
+    arbitrary points: pieces of one segment across several waves, several
+    segments in one wave, more ranges than blocks, and sequences with no
+    blocks at the start, middle and end of the batch."""
+    ctx = [0, 700, 1, 0, 33, 2000, 16, 0]
+    c = make_case(2500 + nw + 10 * kv_dtype, ctx, n_q=16, n_kv=2, d_h=128, kv_dtype=kv_dtype)
+    _say(f"stream ranges nw={nw} kv={kv_dtype}")
+    got, desc = run_case(c, num_partitions=nw)
+    ref = c.oracle_out()
+    for b in (0, 3, 7):
+        assert (got[b] == 0).all()
+    assert max_err(got, ref) < (TOL_8BIT if kv_dtype == FP8 else TOL_16BIT)
+
+
+@pytest.mark.parametrize("d_h", [64, 128])
+@pytest.mark.parametrize("g", [1, 3, 16])
+def test_stream_default_plan_many_short_rows(d_h, g):
+    """A batch of many short, ragged rows on the library's own plan."""
+    r = np.random.default_rng(2600 + d_h + g)
+    ctx = r.integers(0, 300, size=40).tolist()
+    n_kv = 1 if g == 16 else 2
+    c = make_case(2600 + d_h + g, ctx, n_q=g * n_kv, n_kv=n_kv, d_h=d_h)
+    _say(f"stream default plan d_h={d_h} g={g}")
+    got, _ = run_case(c, total_context=int(sum(ctx)))
+    assert max_err(got, c.oracle_out()) < TOL_16BIT
+    got2, _ = run_case(c, num_partitions=97)
+    assert max_err(got2, c.oracle_out()) < TOL_16BIT
+
+
 def test_fp32_query_with_bf16_cache():
     c = make_case(3001, CTX_RAGGED, n_q=8, n_kv=2, d_h=128, q_dtype=F32)
     _say("fp32 q, bf16 cache")
@@ -148,14 +180,15 @@ def test_unmapped_block_poisons_only_its_row(parts):
     assert max_err(got[[0, 1]], ref[[0, 1]]) < TOL_16BIT
 
 
-def test_context_beyond_table_is_nan():
+@pytest.mark.parametrize("parts", [0, 1, 4])
+def test_context_beyond_table_is_nan(parts):
     c = make_case(7201, [40, 20], n_q=4, n_kv=2, d_h=64, max_blocks=3)
     bad = c.ctx.copy()
     bad[1] = 3 * 16 + 1              # more tokens than the table can hold
     c2 = make_case(7201, [40, 20], n_q=4, n_kv=2, d_h=64, max_blocks=3)
     c2.ctx = bad
-    _say("context beyond table")
-    got, _ = run_case(c2, max_context=40)
+    _say(f"context beyond table parts={parts}")
+    got, _ = run_case(c2, max_context=40, num_partitions=parts)
     assert np.isnan(got[1]).all()
     assert max_err(got[0], c.oracle_out()[0]) < TOL_16BIT
 
