@@ -20,7 +20,7 @@ its HIP-event-timed average duration against 8 TB/s), and the CPU baseline
 (the fp64 oracle on the host's cores over the same workload). The oracle
 output is also compared with the GPU output row by row (parity at full size).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -51,8 +51,10 @@ def _pct(xs, q):
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=0.1,
+                    help="seconds of untimed steps before the warmup (clock ramp)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-oracle", action="store_true",
                     help="skip the CPU oracle leg (parity + cpu_baseline)")
@@ -250,7 +252,17 @@ def main(argv=None) -> int:
         append()
         attend()
 
-    _say(f"[bench] plan P={P} blocks/partition={bpp}; warmup {args.warmup}")
+    # Clock settle (untimed): MI355X takes ~15-20 ms of sustained work to
+    # reach its steady clocks; the first steps of a cold GPU run up to 1.5x
+    # slower. Steps run until `--settle` seconds have passed, then the W
+    # counted warmup steps.
+    _say(f"[bench] plan P={P} blocks/partition={bpp}; settle {args.settle} s, "
+         f"warmup {args.warmup}")
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

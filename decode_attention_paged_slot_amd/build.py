@@ -26,7 +26,7 @@ ARCH = os.environ.get("PDA_OFFLOAD_ARCH", "gfx950")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
-          f"-I{CSRC}"]
+          f"-I{CSRC}"] + os.environ.get("PDA_EXTRA_FLAGS", "").split()
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 

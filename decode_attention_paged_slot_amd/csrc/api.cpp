@@ -82,9 +82,10 @@ Plan make_partition_plan(const pda_attn_desc& d) {
 
 // Stream plan (16-bit and 8-bit caches). Measured on MI355X: the step runs
 // at its best when every compute unit holds the same amount of work, and one
-// workgroup of four streaming waves per compute unit already saturates HBM;
-// so the default is 256 workgroups (1024 wave ranges), fewer when the batch
-// has under 8 blocks per range. The block count T is estimated from the
+// workgroup of four streaming waves per compute unit already saturates HBM
+// with a bf16 cache; so the default is 256 workgroups (1024 wave ranges) for
+// bf16 and 512 for 8-bit caches, fewer when the batch has under 8 blocks per
+// range. The block count T is estimated from the
 // host hints (total_context, else B * max_context); the kernel recomputes the
 // exact split from context_lens, so the estimate only tunes the wave count.
 Plan make_stream_plan(const pda_attn_desc& d) {
@@ -99,10 +100,14 @@ Plan make_stream_plan(const pda_attn_desc& d) {
     if (d.num_partitions > 1) {
         nw = d.num_partitions;
     } else {
-        const int64_t wgs = std::max(env_int("PDA_ATTN_WORKGROUPS", 256), 1);
+        // 8-bit caches do twice the conversion and matrix work per byte and
+        // need two workgroups per compute unit to keep HBM busy
+        const bool eight_bit = d.kv_dtype == PDA_FP8_E4M3 || d.kv_dtype == PDA_INT8;
+        const int64_t wgs = std::max(env_int("PDA_ATTN_WORKGROUPS", eight_bit ? 512 : 256), 1);
         const int64_t min_blocks = std::max(env_int("PDA_MIN_BLOCKS_PER_WAVE", 8), 1);
         nw = std::min<int64_t>(4 * wgs, (t_est + min_blocks - 1) / min_blocks);
-        if (nw <= S) return p;   // short contexts: one wave per segment, no merge
+        // short contexts (a few blocks per segment): one wave per segment, no merge
+        if (nw <= S && t_est <= S * 4 * min_blocks) return p;
     }
     nw = std::min<int64_t>(nw, kMaxStreamWaves);
     p.nw = (int32_t)nw;

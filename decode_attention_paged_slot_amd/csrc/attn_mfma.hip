@@ -49,7 +49,11 @@ namespace pda {
 
 namespace {
 
-constexpr int kDepth = 2;   // blocks in flight per wave beyond the one being consumed
+#ifndef PDA_ATTN_DEPTH
+#define PDA_ATTN_DEPTH 2
+#endif
+constexpr int kDepth = PDA_ATTN_DEPTH;   // blocks in flight per wave beyond the one being consumed
+constexpr float kSlack = 8.0f;   // lazy-rescaling threshold (weights < 2^8)
 
 template <int HD, int KV>
 struct Tr {
@@ -90,7 +94,29 @@ __device__ __forceinline__ uint4 ld16_stream(const char* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ float fshfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane
+// rows of a wave) with the gfx950 row swaps: permlane16_swap exchanges rows
+// 1 <-> 0 and 3 <-> 2 between its two operands, permlane32_swap the two
+// halves; with both operands equal, each result pair holds a lane's value
+// and its partner's.
+__device__ __forceinline__ float max_rows4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_rows4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int KV>
 __device__ __forceinline__ bf16x8 kv_operand_from_bytes(uint4 w, int half) {
@@ -359,8 +385,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     };
 
     auto flush = [&](int seg, bool whole) {
-        float l_tot = l_run + fshfl_xor(l_run, 16);
-        l_tot += fshfl_xor(l_tot, 32);
+        float l_tot = sum_rows4(l_run);
         if (piece_bad) l_tot = __builtin_nanf("");
         if (col < g) {
             const int64_t prow = whole ? (int64_t)seg * g + col : ((int64_t)seg + wg) * g + col;
@@ -463,22 +488,30 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             sv[e] = st[e] * mult;
             if (valid < 16 && 4 * grp + e >= valid) sv[e] = -__builtin_inff();
         }
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mx = fmaxf(mx, fshfl_xor(mx, 16));
-        mx = fmaxf(mx, fshfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const float mx = max_rows4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+        // Lazy rescaling: the reference max of a head moves only when the
+        // block's max exceeds it by more than kSlack (log2 units), so the
+        // weights stay below 2^kSlack and the accumulators are rescaled in
+        // the rare blocks where some head's max jumps (the first block of a
+        // piece always sets it). Any reference gives the same softmax: the
+        // partial carries (reference, sum) together.
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+            const float m_new = mx > m_run + kSlack ? mx : m_run;
+            const float alpha = m_run == -__builtin_inff() ? 0.0f
+                                                           : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
         float pe[4], psum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
             psum += pe[e];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
+        l_run += psum;
 
         uint32_t hi16[4], lo16[4];
 #pragma unroll

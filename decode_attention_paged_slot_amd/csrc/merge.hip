@@ -18,6 +18,7 @@ namespace pda {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMergeColumnSplit = 4;   // workgroups per output row when segments have many pieces
 
 __device__ __forceinline__ float block_max(float v, float* red) {
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
@@ -40,19 +41,20 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // Merge of np partials of one output row into `out_row` (HD floats or
-// bf16): partial p has statistics (m, l) at ml + p * sm and output at
-// po + p * so. Phase 1: every thread takes partials p = tid, tid + 256, ...
-// for the block-wide max M and the weights w_p = l_p 2^(m_p - M), kept in
-// LDS. Phase 2: thread (sub, c) accumulates the 4-float column group c of the
-// partials p = sub, sub + SUB, ... (loads are unconditional, so they can all
-// be in flight together; an empty partial's weight is 0 and its data unused);
-// the SUB partial sums are added through LDS.
-template <int HD>
+// bf16), columns [c0 * 4, (c0 + V) * 4) of it: partial p has statistics
+// (m, l) at ml + p * sm and output at po + p * so. Phase 1: every thread takes
+// partials p = tid, tid + 256, ... for the block-wide max M and the weights
+// w_p = l_p 2^(m_p - M), kept in LDS. Phase 2: thread (sub, c) accumulates
+// the 4-float column group c0 + c of the partials p = sub, sub + SUB, ...
+// (loads are unconditional, so they can all be in flight together; an empty
+// partial's weight is 0 and its data unused); the SUB partial sums are added
+// through LDS.
+template <int V>
 __device__ __forceinline__ void merge_row(const float* __restrict__ po, int64_t so,
                                           const float* __restrict__ ml, int64_t sm, int np,
-                                          bool row_bad, void* out_row, int32_t out_dtype,
-                                          float* wsh, float* red, f32x4* acc_sh) {
-    constexpr int V = HD / 4;          // float4 column groups per row
+                                          bool row_bad, int c0, void* out_row,
+                                          int32_t out_dtype, float* wsh, float* red,
+                                          f32x4* acc_sh) {
     constexpr int SUB = kThreads / V;  // partial subsets
     float mloc = -__builtin_inff();
     for (int p = threadIdx.x; p < np; p += kThreads) {
@@ -72,7 +74,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ po, int64_t 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
     for (int p = sub; p < np; p += SUB) {
-        const f32x4 o = *((const f32x4*)(po + p * so) + c);
+        const f32x4 o = *((const f32x4*)(po + p * so) + c0 + c);
         const float w = wsh[p];
         if (w != 0.0f) acc += w * o;
     }
@@ -89,12 +91,12 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ po, int64_t 
         if (row_bad) r = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                                __builtin_nanf("")};
         if (out_dtype == DT_F32) {
-            *((f32x4*)out_row + c) = r;
+            *((f32x4*)out_row + c0 + c) = r;
         } else {
             uint2 h;
             h.x = f32_to_bf16_rne(r[0]) | (f32_to_bf16_rne(r[1]) << 16);
             h.y = f32_to_bf16_rne(r[2]) | (f32_to_bf16_rne(r[3]) << 16);
-            *((uint2*)out_row + c) = h;
+            *((uint2*)out_row + c0 + c) = h;
         }
     }
 }
@@ -123,22 +125,26 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
         np = min(P, (nblk + bpp - 1) / bpp);
     }
     char* orow = (char*)out + row * HD * (out_dtype == DT_F32 ? 4 : 2);
-    merge_row<HD>(part_o + row * (int64_t)P * HD, HD, part_ml + row * (int64_t)P * 2, 2, np,
-                  row_bad, orow, out_dtype, wsh, red, acc_sh);
+    merge_row<HD / 4>(part_o + row * (int64_t)P * HD, HD, part_ml + row * (int64_t)P * 2, 2, np,
+                      row_bad, 0, orow, out_dtype, wsh, red, acc_sh);
 }
 
 // Stream layout (attention kernel's split mode): output row r = seg * g + hh
 // of segment seg; the pieces of a split segment sit in slots seg + w for the
 // waves w in seg_info[seg] = (first, last), piece row (seg + w) * g + hh.
 // Segments with a single piece (written by the attention kernel directly)
-// or none (zero / NaN rows, also written there) are skipped.
-template <int HD>
+// or none (zero / NaN rows, also written there) are skipped. With CS > 1
+// workgroups per row (grid.y), workgroup (row, cs) handles the cs-th of CS
+// column ranges, so rows with many pieces are spread over several compute
+// units. The weights live in dynamic LDS sized for the wave count.
+template <int HD, int CS>
 __global__ void __launch_bounds__(kThreads) k_merge_stream(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            const int2* __restrict__ seg_info,
                                                            int32_t g, void* out,
                                                            int32_t out_dtype) {
-    __shared__ float wsh[kMaxStreamWaves];
+    constexpr int V = HD / 4 / CS;
+    extern __shared__ float wsh[];
     __shared__ float red[4];
     __shared__ f32x4 acc_sh[kThreads];
     const int64_t row = blockIdx.x;
@@ -149,8 +155,8 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(const float* __restri
     if (np <= 1) return;
     const int64_t prow0 = (seg + info.x) * g + hh;
     char* orow = (char*)out + row * HD * (out_dtype == DT_F32 ? 4 : 2);
-    merge_row<HD>(part_o + prow0 * HD, (int64_t)g * HD, part_ml + prow0 * 2, (int64_t)g * 2,
-                  np, false, orow, out_dtype, wsh, red, acc_sh);
+    merge_row<V>(part_o + prow0 * HD, (int64_t)g * HD, part_ml + prow0 * 2, (int64_t)g * 2, np,
+                 false, (int)blockIdx.y * V, orow, out_dtype, wsh, red, acc_sh);
 }
 
 hipError_t launch_merge(const float* part_o, const float* part_ml, const int32_t* context_lens,
@@ -176,12 +182,21 @@ hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.n_q;
     if (rows == 0) return hipSuccess;
-    if (a.d_h == 128)
-        hipLaunchKernelGGL((k_merge_stream<128>), dim3(rows), dim3(kThreads), 0, s, a.part_o,
-                           a.part_ml, a.seg_info, a.g, a.out, a.out_dtype);
-    else
-        hipLaunchKernelGGL((k_merge_stream<64>), dim3(rows), dim3(kThreads), 0, s, a.part_o,
-                           a.part_ml, a.seg_info, a.g, a.out, a.out_dtype);
+    const size_t lds = (size_t)a.nw * sizeof(float);
+    // split a row's columns over several workgroups only when segments
+    // average many pieces (long sequences in a small batch)
+    const bool wide = (int64_t)a.nw >= 64 * (int64_t)a.B * a.n_kv;
+#define PDA_MS(HD, CS)                                                                       \
+    hipLaunchKernelGGL((k_merge_stream<HD, CS>), dim3(rows, CS), dim3(kThreads), lds, s,    \
+                       a.part_o, a.part_ml, a.seg_info, a.g, a.out, a.out_dtype)
+    if (a.d_h == 128) {
+        if (wide) PDA_MS(128, kMergeColumnSplit);
+        else PDA_MS(128, 1);
+    } else {
+        if (wide) PDA_MS(64, kMergeColumnSplit);
+        else PDA_MS(64, 1);
+    }
+#undef PDA_MS
     return hipGetLastError();
 }
 
