@@ -63,6 +63,7 @@ struct AttnArgs {
     int32_t kv_dtype, q_dtype, out_dtype;
     int32_t P, bpp;
     int32_t nw, split;
+    int32_t reuse_blocks;   // leading logical blocks read with cache-retaining loads
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s);

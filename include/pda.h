@@ -196,6 +196,13 @@ typedef struct pda_attn_desc {
     int32_t max_context;        /* host-side bound on context_lens, sizes the split */
     int32_t num_partitions;     /* split-KV partitions: 0 = choose, 1 = none, k = at most k */
     int64_t total_context;      /* optional sum of context_lens (0 = unknown); tunes the split */
+    int32_t reuse_prefix_blocks; /* cache hint: the first reuse_prefix_blocks logical blocks
+                                    of every row are read with cache-retaining loads (blocks
+                                    shared by many rows, e.g. a common prompt prefix, are then
+                                    served from L2 / Infinity Cache after their first read);
+                                    all other blocks are streamed with non-temporal loads.
+                                    0 = stream everything. Affects speed only, never results. */
+    int32_t reserved;           /* must be 0 */
 } pda_attn_desc;
 
 /* Workspace bytes pda_paged_decode_attn needs for this descriptor (0 when it

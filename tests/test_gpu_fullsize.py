@@ -83,7 +83,8 @@ def test_full_size_workload(name):
     sl = torch.from_numpy(slots).to(dev)
     out = torch.full((w.B, w.n_q, w.d_h), float("nan"), device=dev)
     desc = pda.attn_desc(inp.q, inp.k_cache, bt, max_context=int(inp.ctx.max()),
-                         kv_dtype=w.kv_dtype, total_context=int(inp.ctx.sum()))
+                         kv_dtype=w.kv_dtype, total_context=int(inp.ctx.sum()),
+                         reuse_prefix_blocks=w.shared_prefix_tokens // w.block_size)
     ws = pda.workspace_for(desc, dev)
     if quant:
         pda.kv_append_quant(inp.k_new, inp.v_new, sl, inp.k_cache, inp.v_cache, inp.k_scale,

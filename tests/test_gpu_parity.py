@@ -141,6 +141,19 @@ def test_prefix_aliasing_bit_identical():
     assert max_err(a, c.oracle_out()) < TOL_16BIT
 
 
+@pytest.mark.parametrize("kv_dtype", [BF16, FP8])
+def test_reuse_hint_changes_nothing(kv_dtype):
+    """The shared-prefix cache hint only picks the load flavour: results are
+    bit-identical for any value."""
+    c = make_case(6301 + kv_dtype, [300, 70, 33, 17, 1, 0], n_q=8, n_kv=2, d_h=128,
+                  shared_prefix_blocks=4, kv_dtype=kv_dtype)
+    _say(f"reuse hint kv={kv_dtype}")
+    base, _ = run_case(c, num_partitions=5)
+    for reuse in (1, 4, 1000):
+        got, _ = run_case(c, num_partitions=5, reuse_prefix_blocks=reuse)
+        assert (got == base).all()
+
+
 def test_rerun_deterministic():
     c = make_case(6201, CTX_RAGGED, n_q=16, n_kv=2, d_h=128)
     _say("determinism")
