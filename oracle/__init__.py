@@ -13,7 +13,9 @@ Contents, each written from the pages' statement of the method:
                        allocation and lookup, not the attention formula ("9
                        Decode and KV Cache", section 9.5); GQA maps query head
                        h to KV head h // g (kv-cache tag page, GQA teaser; SoK
-                       paper section 1.1).
+                       paper section 1.1). Optional sliding window with
+                       attention sinks (section 9.7; sink and sliding-window
+                       teasers on the tag page).
 * `physical_location`, `slot_of` -- the logical position -> (physical block,
                        offset) translation of the worked example "PagedAttention
                        block lookup" (section 9.5), and the flat slot index
@@ -58,6 +60,7 @@ def load(path: str) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     L.or_decode.restype = ctypes.c_int
     L.or_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
@@ -105,12 +108,14 @@ def fp8_decode_table() -> np.ndarray:
 # ------------------------------------------------------------------ attention
 def paged_attn(q, k_cache, v_cache, block_table, context_lens, scale, *, n_q, n_kv,
                q_dtype, kv_dtype, k_scale=None, v_scale=None, rows=None, t_begin=-1,
-               t_end=-1, nthreads=0, _lib=None):
+               t_end=-1, window=0, sinks=0, nthreads=0, _lib=None):
     """fp64 paged decode attention (see pda_oracle.c for the definition).
 
     Returns (out [n_rows, d_h], m [n_rows], z [n_rows], n_bad). `rows` lists
     flat (b * n_q + h) indices; None computes all. m is the max scaled score
-    (natural-log units), z = sum_t exp(s_t - m)."""
+    (natural-log units), z = sum_t exp(s_t - m). With window > 0 only the
+    positions t < sinks or t >= n - window of each row are attended (sliding
+    window with attention sinks, "9 Decode and KV Cache", section 9.7)."""
     q = np.ascontiguousarray(q)
     k_cache = np.ascontiguousarray(k_cache)
     v_cache = np.ascontiguousarray(v_cache)
@@ -136,7 +141,8 @@ def paged_attn(q, k_cache, v_cache, block_table, context_lens, scale, *, n_q, n_
     bad = L.or_paged_attn(B, n_q, n_kv, d_h, bs, num_blocks, bt.shape[1], _ptr(q), q_dtype,
                           _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(ks), _ptr(vs),
                           _ptr(bt), _ptr(cl), float(scale), _ptr(r), n_rows, int(t_begin),
-                          int(t_end), _ptr(out), _ptr(m), _ptr(z), int(nthreads))
+                          int(t_end), int(window), int(sinks), _ptr(out), _ptr(m), _ptr(z),
+                          int(nthreads))
     if bad < 0:
         raise ValueError("oracle: bad arguments")
     return out, m, z, int(bad)

@@ -25,8 +25,28 @@ def gather_contiguous(cache_f64: np.ndarray, table_row: np.ndarray, n: int, bloc
     return np.stack(rows) if rows else np.zeros((0,) + cache_f64.shape[1:2] + cache_f64.shape[3:])
 
 
+def gather_positions(cache_f64: np.ndarray, table_row: np.ndarray, positions, block_size: int):
+    """Rows of the listed logical positions only (the others are never looked up)."""
+    rows = []
+    for t in positions:
+        pb = int(table_row[t // block_size])
+        if pb < 0 or pb >= cache_f64.shape[0]:
+            raise KeyError(t // block_size)
+        rows.append(cache_f64[pb, :, t % block_size, :])
+    return np.stack(rows)
+
+
+def attended_positions(n: int, window: int = 0, sinks: int = 0):
+    """Logical positions of an n-token row that enter the softmax: all of
+    them, or with a sliding window of `window` tokens the last `window` plus
+    the first `sinks` (attention sinks)."""
+    if window <= 0 or n <= sinks + window:
+        return list(range(n))
+    return list(range(min(sinks, n))) + list(range(n - window, n))
+
+
 def attention(q, k_cache, v_cache, block_table, context_lens, scale, *, n_q, n_kv, q_dtype,
-              kv_dtype, k_scale=None, v_scale=None):
+              kv_dtype, k_scale=None, v_scale=None, window=0, sinks=0):
     """[B, n_q, d_h] fp64 outputs for every row."""
     qd = decode(q, q_dtype)
     kd = decode(k_cache, kv_dtype)
@@ -42,8 +62,9 @@ def attention(q, k_cache, v_cache, block_table, context_lens, scale, *, n_q, n_k
         n = int(context_lens[b])
         if n == 0:
             continue
-        K = gather_contiguous(kd, block_table[b], n, bs)   # [n, n_kv, d_h]
-        V = gather_contiguous(vd, block_table[b], n, bs)
+        idx = attended_positions(n, window, sinks)
+        K = gather_positions(kd, block_table[b], idx, bs)   # [len(idx), n_kv, d_h]
+        V = gather_positions(vd, block_table[b], idx, bs)
         for h in range(n_q):
             j = h // g
             s = (K[:, j, :] @ qd[b, h]) * scale

@@ -35,6 +35,13 @@
  * range of logical positions; the partial result (normalised output, max
  * score m, and Z) is what a split-KV partition holds before the merge.
  *
+ * Sliding window with attention sinks (long-context variants of "9 Decode and
+ * KV Cache", section 9.7: a sliding window keeps only the most recent W
+ * tokens; attention sinks keep the first few tokens as well; the sink and
+ * sliding-window teasers on the kv-cache tag page): with window W > 0 and S
+ * sink tokens, only positions t with t < S or t >= n - W enter the softmax;
+ * the others are not looked up at all. W = 0 attends to every position.
+ *
  * Element decodes (written from the format definitions, not from any library):
  *   f32  : IEEE binary32 as stored.
  *   bf16 : the upper 16 bits of a binary32.
@@ -86,6 +93,11 @@ static double or_dec_int8(const void* p, int64_t i) {
 
 typedef double (*or_dec_fn)(const void*, int64_t);
 
+/* Is logical position t of an n-token row attended (window / sink rule)? */
+static int or_attended(int64_t t, int64_t n, int64_t window, int64_t sinks) {
+    return window <= 0 || t < sinks || t >= n - window;
+}
+
 static or_dec_fn or_decoder(int dtype) {
     switch (dtype) {
     case OR_F32: return or_dec_f32;
@@ -112,6 +124,7 @@ int or_decode(const void* src, int dtype, int64_t n, double* dst) {
  *   block_table [B][max_blocks] int32, context_lens [B] int32
  *   rows    list of (b * n_q + h) to compute, or NULL for all B*n_q rows
  *   t_begin, t_end  token window (t_end < 0: to the end of each row)
+ *   window, sinks   attend only to t < sinks or t >= n - window (window 0: all)
  *   out     [n_rows][d_h] fp64; m_out, z_out [n_rows] (either may be NULL)
  * Returns the number of rows that hit an unmapped block or an invalid
  * context length (their outputs are NaN), or -1 on a bad argument.
@@ -121,8 +134,10 @@ int64_t or_paged_attn(int B, int n_q, int n_kv, int d_h, int bs, int num_blocks,
                       const float* k_scale, const float* v_scale,
                       const int32_t* block_table, const int32_t* context_lens, double scale,
                       const int64_t* rows, int64_t n_rows, int64_t t_begin, int64_t t_end,
+                      int64_t window, int64_t sinks,
                       double* out, double* m_out, double* z_out, int nthreads) {
     if (B <= 0 || n_q <= 0 || n_kv <= 0 || d_h <= 0 || bs <= 0 || n_q % n_kv) return -1;
+    if (window < 0 || sinks < 0) return -1;
     or_dec_fn dq = or_decoder(q_dtype), dkv = or_decoder(kv_dtype);
     if (!dq || !dkv) return -1;
     int quant = (kv_dtype == OR_FP8 || kv_dtype == OR_INT8);
@@ -172,6 +187,7 @@ int64_t or_paged_attn(int B, int n_q, int n_kv, int d_h, int bs, int num_blocks,
             /* scores, checking every lookup */
             int unmapped = 0;
             for (int64_t t = lo; t < hi && !unmapped; ++t) {
+                if (!or_attended(t, n, window, sinks)) continue;
                 const int32_t pb = block_table[(int64_t)b * max_blocks + t / bs];
                 if (pb < 0 || pb >= num_blocks) { unmapped = 1; break; }
                 const int64_t base = (((int64_t)pb * n_kv + j) * bs + t % bs) * d_h;
@@ -190,6 +206,7 @@ int64_t or_paged_attn(int B, int n_q, int n_kv, int d_h, int bs, int num_blocks,
             /* pass 1: maximum */
             double m = -INFINITY;
             for (int64_t t = lo; t < hi; ++t) {
+                if (!or_attended(t, n, window, sinks)) continue;
                 const double x = s[t - lo];
                 if (isnan(x) || isnan(m)) m = NAN; /* a NaN key poisons the row */
                 else if (x > m) m = x;
@@ -198,12 +215,19 @@ int64_t or_paged_attn(int B, int n_q, int n_kv, int d_h, int bs, int num_blocks,
             double z = 0.0;
             for (int d = 0; d < d_h; ++d) acc[d] = 0.0;
             for (int64_t t = lo; t < hi; ++t) {
+                if (!or_attended(t, n, window, sinks)) continue;
                 const int32_t pb = block_table[(int64_t)b * max_blocks + t / bs];
                 const int64_t base = (((int64_t)pb * n_kv + j) * bs + t % bs) * d_h;
                 const double vs = quant ? (double)v_scale[(int64_t)pb * n_kv + j] : 1.0;
                 const double w = exp(s[t - lo] - m);
                 z += w;
                 for (int d = 0; d < d_h; ++d) acc[d] += w * (vs * dkv(v, base + d));
+            }
+            if (z == 0.0) { /* no attended position in [lo, hi): an empty partial */
+                for (int d = 0; d < d_h; ++d) o[d] = 0.0;
+                if (m_out) m_out[r] = -INFINITY;
+                if (z_out) z_out[r] = 0.0;
+                continue;
             }
             for (int d = 0; d < d_h; ++d) o[d] = acc[d] / z;
             if (m_out) m_out[r] = m;

@@ -317,8 +317,53 @@ def pin_errors(paged):
     return fails
 
 
+def pin_window(paged):
+    """Sliding window with attention sinks ("9 Decode and KV Cache", section
+    9.7): positions t < S or t >= n - W of each row."""
+    fails = []
+    c = make_case(81, [100, 37, 200, 1, 16], n_q=4, n_kv=2, d_h=32, kv_dtype=F32, q_dtype=F32)
+    full = paged(c)[0]
+    # a window covering the whole row, or sinks + window covering it: no change
+    if not (paged(c, window=200)[0] == full).all():
+        fails.append("window >= n")
+    if not (paged(c, window=150, sinks=60)[0] == full).all():
+        fails.append("sinks + window >= n")
+    # window 1, no sinks: the newest token's value, exactly
+    one = paged(c, window=1)[0].reshape(c.B, c.n_q, c.d_h)
+    vd = oracle.decode(c.v, F32)
+    for b, n in enumerate(c.ctx):
+        last = vd[c.table[b, (n - 1) // 16], :, (n - 1) % 16, :]
+        if not (one[b] == np.repeat(last, c.g, axis=0)).all():
+            fails.append(f"window 1 row {b}")
+    # the independent gather-then-softmax reference, windows starting mid-block
+    # and sinks crossing a block boundary
+    for (w, sk) in [(5, 0), (17, 3), (33, 20), (64, 1), (3, 16)]:
+        ours = paged(c, window=w, sinks=sk)[0].reshape(c.B, c.n_q, c.d_h)
+        ref = brute.attention(c.q, c.k, c.v, c.table, c.ctx, c.scale, n_q=c.n_q, n_kv=c.n_kv,
+                              q_dtype=c.q_dtype, kv_dtype=c.kv_dtype, window=w, sinks=sk)
+        if not np.allclose(ours, ref, atol=1e-12, rtol=1e-12):
+            fails.append(f"window brute force ({w}, {sk})")
+    # unattended positions are never read: NaN there, and an unmapped block
+    # that holds only unattended positions, change nothing
+    w, sk = 20, 4
+    ref = paged(c, window=w, sinks=sk)[0]
+    c2 = make_case(81, [100, 37, 200, 1, 16], n_q=4, n_kv=2, d_h=32, kv_dtype=F32, q_dtype=F32)
+    for b, n in enumerate(c2.ctx):
+        for t in range(n):
+            if not (t < sk or t >= n - w):
+                pb = c2.table[b, t // 16]
+                c2.k[pb, :, t % 16, :] = np.nan
+                c2.v[pb, :, t % 16, :] = np.nan
+    c2.table = c2.table.copy()
+    c2.table[2, 5] = -1          # row 2 (200 tokens): block 5 holds positions 80..95 only
+    got, _, _, bad = paged(c2, window=w, sinks=sk)
+    if bad != 0 or not (got == ref).all():
+        fails.append("unattended positions read")
+    return fails
+
+
 ALL_PINS = [pin_closed_forms, pin_brute_force, pin_gqa_is_repeated_mha, pin_invariances,
-            pin_split_merge, pin_errors]
+            pin_split_merge, pin_errors, pin_window]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -421,6 +466,9 @@ MUTANTS = {
                                    "block_table[(int64_t)b * max_blocks + t % bs];\n                if (pb < 0"),
     "value scale dropped": ("const double vs = quant ? (double)v_scale[(int64_t)pb * n_kv + j] : 1.0;",
                             "const double vs = 1.0;"),
+    "window off by one": ("t >= n - window;", "t > n - window;"),
+    "sinks dropped": ("window <= 0 || t < sinks || t >= n - window;",
+                      "window <= 0 || t >= n - window;"),
 }
 
 
