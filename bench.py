@@ -107,7 +107,8 @@ def oracle_leg(w, inp, table, slots, shared, host):
     out, _, _, bad = oracle.paged_attn(host["q"], k, v, otable, inp.ctx, w.softmax_scale,
                                        n_q=w.n_q, n_kv=w.n_kv, q_dtype=w.q_dtype,
                                        kv_dtype=w.kv_dtype, k_scale=host.get("ks"),
-                                       v_scale=host.get("vs"))
+                                       v_scale=host.get("vs"), window=w.attn_window,
+                                       sinks=w.attn_sinks)
     secs = time.perf_counter() - t0
     del k, v
     return {"secs": secs, "threads": oracle.num_threads(), "bad_rows": bad,
@@ -229,7 +230,8 @@ def main(argv=None) -> int:
     reuse = w.shared_prefix_tokens // w.block_size
     desc = pda.attn_desc(inp.q, inp.k_cache, bt, max_context=int(inp.ctx.max()),
                          kv_dtype=w.kv_dtype, num_partitions=args.num_partitions,
-                         total_context=int(inp.ctx.sum()), reuse_prefix_blocks=reuse)
+                         total_context=int(inp.ctx.sum()), reuse_prefix_blocks=reuse,
+                         window=w.attn_window, sink_tokens=w.attn_sinks)
     P, bpp = pda.attn_plan(desc)
     ws = pda.workspace_for(desc, dev)
     scale = w.softmax_scale
@@ -324,7 +326,8 @@ def main(argv=None) -> int:
     sb = acc.step_bytes(inp.ctx, n_q=w.n_q, n_kv=w.n_kv, d_h=w.d_h, block_size=w.block_size,
                         kv_dtype=w.kv_dtype, q_dtype=w.q_dtype,
                         new_dtype=synth.BF16 if w.kv_dtype != synth.F32 else synth.F32,
-                        shared_prefix_blocks=inp.shared_ids_count)
+                        shared_prefix_blocks=inp.shared_ids_count, window=w.attn_window,
+                        sinks=w.attn_sinks)
     att_avg = float(np.median(att_ms))
     achieved = sb.attention / (att_avg * 1e-3) / 1e9
     value = sb.step / (ms_per_step * 1e-3) / 1e9
@@ -347,7 +350,10 @@ def main(argv=None) -> int:
         cpu = {"value": round(sb.attention / info["secs"] / 1e9, 4), "unit": "GB/s",
                "cores": int(info["threads"]), "kind": "oracle",
                "sample": (f"whole workload ({w.B} sequences x {w.n_q} query heads, "
-                          f"{int(inp.ctx.sum())} cached tokens); fp64 two-pass oracle, "
+                          f"{int(inp.ctx.sum())} cached tokens"
+                          + (f", window {w.attn_window} + {w.attn_sinks} sinks"
+                             if w.attn_window else "")
+                          + f"); fp64 two-pass oracle, "
                           f"{info['secs']:.2f} s wall on {info['threads']} threads")}
         _say(f"[bench] parity max-abs {err:.3g} (tol {tol}); oracle {info['secs']:.2f} s")
 
@@ -372,6 +378,7 @@ def main(argv=None) -> int:
             "context_min": int(inp.ctx.min()), "context_max": int(inp.ctx.max()),
             "total_context": int(inp.ctx.sum()), "pool_blocks": int(inp.num_blocks),
             "num_partitions": P, "blocks_per_partition": bpp, "reuse_prefix_blocks": reuse,
+            "window": w.attn_window, "sink_tokens": w.attn_sinks,
             "parallelism": "none (1 GPU)",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),

@@ -95,15 +95,34 @@ class StepBytes:
         return self.attention + self.append_read + self.append_write
 
 
+def attended_tokens(n: int, window: int = 0, sinks: int = 0) -> int:
+    """Positions of an n-token row that attention reads: all of them, or with
+    a sliding window the last `window` plus the first `sinks`."""
+    if window <= 0 or n <= sinks + window:
+        return n
+    return sinks + window
+
+
+def attended_blocks(n: int, block_size: int, window: int = 0, sinks: int = 0) -> int:
+    """Blocks holding at least one attended position of an n-token row."""
+    nblk = -(-n // block_size)
+    if window <= 0 or n <= sinks + window:
+        return nblk
+    sb = -(-sinks // block_size)
+    return sb + nblk - max((n - window) // block_size, sb)
+
+
 def step_bytes(context_lens: Sequence[int], *, n_q: int, n_kv: int, d_h: int, block_size: int,
                kv_dtype: int, q_dtype: int, out_bytes: int = 4, new_dtype: Optional[int] = None,
-               appended_tokens: Optional[int] = None, shared_prefix_blocks: int = 0) -> StepBytes:
-    """Bytes one decode step must move (SoK appendix A.1 accounting)."""
+               appended_tokens: Optional[int] = None, shared_prefix_blocks: int = 0,
+               window: int = 0, sinks: int = 0) -> StepBytes:
+    """Bytes one decode step must move (SoK appendix A.1 accounting); with a
+    sliding window only the attended positions count."""
     w_kv = ELEM_BYTES[kv_dtype]
     w_q = ELEM_BYTES[q_dtype]
     B = len(context_lens)
-    tokens = sum(int(n) for n in context_lens)
-    blocks = [-(-int(n) // block_size) for n in context_lens]
+    tokens = sum(attended_tokens(int(n), window, sinks) for n in context_lens)
+    blocks = [attended_blocks(int(n), block_size, window, sinks) for n in context_lens]
     kv = 2 * tokens * n_kv * d_h * w_kv
     if shared_prefix_blocks:
         shared = [min(shared_prefix_blocks, max(nb - 1, 0)) for nb in blocks]

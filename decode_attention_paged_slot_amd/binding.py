@@ -60,7 +60,8 @@ class AttnDesc(ctypes.Structure):
                 ("kv_dtype", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("max_context", ctypes.c_int32),
                 ("num_partitions", ctypes.c_int32), ("total_context", ctypes.c_int64),
-                ("reuse_prefix_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("reuse_prefix_blocks", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("sink_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -164,14 +165,15 @@ def kv_append_quant(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_sca
 # --------------------------------------------------------------- attention
 def attn_desc(q, k_cache, block_table, *, max_context: int, out_dtype: int = F32,
               kv_dtype: Optional[int] = None, num_partitions: int = 0,
-              total_context: int = 0, reuse_prefix_blocks: int = 0) -> AttnDesc:
+              total_context: int = 0, reuse_prefix_blocks: int = 0, window: int = 0,
+              sink_tokens: int = 0) -> AttnDesc:
     B, n_q, d_h = q.shape
     nb, n_kv, bs, d2 = k_cache.shape
     assert d2 == d_h
     kvd = kv_dtype if kv_dtype is not None else dtype_code(k_cache)
     return AttnDesc(B, n_q, n_kv, d_h, bs, int(block_table.shape[1]), nb, kvd, dtype_code(q),
                     out_dtype, int(max_context), int(num_partitions), int(total_context),
-                    int(reuse_prefix_blocks), 0)
+                    int(reuse_prefix_blocks), int(window), int(sink_tokens), 0)
 
 
 def attn_workspace_size(desc: AttnDesc) -> int:
@@ -200,12 +202,14 @@ def workspace_for(desc: AttnDesc, device):
 def paged_decode_attn(q, k_cache, v_cache, block_table, context_lens, scale: float, out, *,
                       desc: Optional[AttnDesc] = None, workspace=None, max_context: int = 0,
                       num_partitions: int = 0, total_context: int = 0,
-                      reuse_prefix_blocks: int = 0, stream=None) -> None:
+                      reuse_prefix_blocks: int = 0, window: int = 0, sink_tokens: int = 0,
+                      stream=None) -> None:
     """pda_paged_decode_attn (f32 / bf16 caches). `out` [B, n_q, d_h] f32 or bf16."""
     if desc is None:
         desc = attn_desc(q, k_cache, block_table, max_context=max_context,
                          out_dtype=dtype_code(out), num_partitions=num_partitions,
-                         total_context=total_context, reuse_prefix_blocks=reuse_prefix_blocks)
+                         total_context=total_context, reuse_prefix_blocks=reuse_prefix_blocks,
+                         window=window, sink_tokens=sink_tokens)
     if workspace is None:
         workspace = workspace_for(desc, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -220,14 +224,15 @@ def paged_decode_attn_quant(q, k_cache, v_cache, k_scale, v_scale, block_table, 
                             desc: Optional[AttnDesc] = None, workspace=None,
                             max_context: int = 0, num_partitions: int = 0,
                             total_context: int = 0, reuse_prefix_blocks: int = 0,
-                            stream=None) -> None:
+                            window: int = 0, sink_tokens: int = 0, stream=None) -> None:
     """pda_paged_decode_attn_quant (fp8 e4m3 / int8 caches with per-(block, head)
     fp32 scales [NB, n_kv])."""
     if desc is None:
         desc = attn_desc(q, k_cache, block_table, max_context=max_context,
                          out_dtype=dtype_code(out), kv_dtype=kv_dtype,
                          num_partitions=num_partitions, total_context=total_context,
-                         reuse_prefix_blocks=reuse_prefix_blocks)
+                         reuse_prefix_blocks=reuse_prefix_blocks, window=window,
+                         sink_tokens=sink_tokens)
     if workspace is None:
         workspace = workspace_for(desc, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

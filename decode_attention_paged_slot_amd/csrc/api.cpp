@@ -172,7 +172,7 @@ int32_t check_attn_desc(const pda_attn_desc* d, bool quant) {
     }
     if (d->max_blocks_per_seq <= 0 || d->num_blocks <= 0 || d->max_context < 0 ||
         d->num_partitions < 0 || d->total_context < 0 || d->reuse_prefix_blocks < 0 ||
-        d->reserved != 0) {
+        d->window < 0 || d->sink_tokens < 0 || d->reserved != 0) {
         set_error("bad sizes: max_blocks_per_seq=%d num_blocks=%d max_context=%d",
                   d->max_blocks_per_seq, d->num_blocks, d->max_context);
         return PDA_EINVAL;
@@ -291,6 +291,8 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     a.nw = plan.nw;
     a.split = plan.split;
     a.reuse_blocks = d->reuse_prefix_blocks;
+    a.window = d->window;
+    a.sinks = d->window > 0 ? d->sink_tokens : 0;
     hipError_t e;
     if (plan.stream) {
         e = launch_attn_mfma(a, s);

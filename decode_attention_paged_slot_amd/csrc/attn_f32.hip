@@ -3,7 +3,8 @@
 // Same method and the same split-KV contract as the matrix-core kernel
 // (sections 9.4-9.5 of "9 Decode and KV Cache"): token t of row b is read at
 // (block_table[b][t / 16], t % 16), s_t = scale * q . k_t, online softmax,
-// sum of p_t v_t. Here everything stays in fp32 FMAs; this path serves fp32
+// sum of p_t v_t, over the attended positions (all, or a sliding window with
+// sinks, section 9.7). Here everything stays in fp32 FMAs; this path serves fp32
 // caches (small, latency-bound workloads), so it favours plainness.
 //
 // grid = (P partitions, n_q, B); one workgroup (4 waves) per query head and
@@ -71,16 +72,20 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_f32(AttnArgs a) {
     const int64_t tile = 16 * HD;   // floats per (block, head) tile
 
     for (int kb = blk0 + wave; kb < blk1; kb += 4) {
+        // attended positions of the block (all t < n, or the window / sinks);
+        // a block without any is never looked up
+        const uint32_t bm = block_token_mask(kb, n, a.window, a.sinks);
+        if (bm == 0) continue;
         const int pb = a.block_table[(int64_t)b * a.max_blocks + kb];
         if (pb < 0 || pb >= a.num_blocks) { bad = true; break; }
-        const int valid = min(16, n - 16 * kb);
+        const bool live = (bm >> t) & 1u;
         const float* kt = (const float*)a.k + ((int64_t)pb * a.n_kv + j) * tile + t * HD;
         const float* vt = (const float*)a.v + ((int64_t)pb * a.n_kv + j) * tile + t * HD;
         float kv[NV][4], vv[NV][4];
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             float4 x = make_float4(0, 0, 0, 0), y = make_float4(0, 0, 0, 0);
-            if (t < valid) {
+            if (live) {
                 x = *(const float4*)(kt + 4 * (part + 4 * k));
                 y = *(const float4*)(vt + 4 * (part + 4 * k));
             }
@@ -94,7 +99,7 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_f32(AttnArgs a) {
             for (int e = 0; e < 4; ++e) dot = fmaf(q[k][e], kv[k][e], dot);
         dot += fshfl_xor(dot, 1);
         dot += fshfl_xor(dot, 2);
-        const float s = t < valid ? dot * a.scale_log2 : -__builtin_inff();
+        const float s = live ? dot * a.scale_log2 : -__builtin_inff();
         float mx = s;
         mx = fmaxf(mx, fshfl_xor(mx, 4));
         mx = fmaxf(mx, fshfl_xor(mx, 8));

@@ -137,12 +137,14 @@ __device__ __forceinline__ bf16x8 kv_operand_from_bytes(uint4 w, int half) {
 
 
 // Per-block metadata, lane i of a 64-block batch describing block i.
-//   info bits 0-4 valid tokens (1..16), bit 5 first block of its segment,
-//   bit 6 last block of its segment, bit 7 shared (cache-retaining loads),
-//   bits 8.. segment index.
+//   info bit 5 first block of its segment, bit 6 last block of its
+//   segment, bit 7 shared (cache-retaining loads), bits 8.. segment index.
+// A segment lists only the blocks holding attended positions (all blocks of
+// the row, or its sink and window blocks with a sliding window).
 struct Meta {
     int id;      // physical block, or -1 when the table entry is unmapped
     int info;
+    int mask;    // attended positions of the block (bit k: token k)
     float ksc, vsc;
 };
 
@@ -175,7 +177,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
                 const int n = a.context_lens[b];
                 const bool bad = n < 0 || n > a.max_blocks * 16;
                 nn[b] = bad ? -1 : n;
-                local += bad ? 0 : (n + 15) >> 4;
+                local += bad ? 0 : row_blocks(n, a.window, a.sinks).count;
             }
         }
         int incl = local;
@@ -192,7 +194,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             const int b = r0 + r;
             if (b < B) {
                 pre[b] = run;
-                run += nn[b] < 0 ? 0 : (nn[b] + 15) >> 4;
+                run += nn[b] < 0 ? 0 : row_blocks(nn[b], a.window, a.sinks).count;
             }
         }
         if (threadIdx.x == kAttnThreads - 1) pre[B] = run;
@@ -255,7 +257,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
 
     // ---- per-block metadata of batch `batch` (64 blocks from lo + 64 * batch)
     auto load_meta = [&](int batch) {
-        Meta m{-1, 0, 1.0f, 1.0f};
+        Meta m{-1, 0, 0, 1.0f, 1.0f};
         const int64_t f = lo + (int64_t)batch * 64 + lane;
         if (f < hi) {
             const int x = (int)f;
@@ -269,14 +271,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             const int nb = pre[b + 1] - pre[b];
             const int r0 = x - n_kv * pre[b];
             const int j = r0 / nb;
-            const int blk = r0 - j * nb;
+            const int bl = r0 - j * nb;   // attended-block index within the row
+            const int blk = row_block_logical(row_blocks(nn[b], a.window, a.sinks), bl);
             int id = a.block_table[(int64_t)b * a.max_blocks + blk];
             if (id < 0 || id >= a.num_blocks) id = -1;
-            const int valid = min(16, nn[b] - 16 * blk);
             const int seg = b * n_kv + j;
             m.id = id;
-            m.info = valid | ((blk == 0) << 5) | ((blk == nb - 1) << 6) |
-                     ((blk < a.reuse_blocks) << 7) | (seg << 8);
+            m.info = ((bl == 0) << 5) | ((bl == nb - 1) << 6) | ((blk < a.reuse_blocks) << 7) |
+                     (seg << 8);
+            m.mask = (int)block_token_mask(blk, nn[b], a.window, a.sinks);
             if (QUANT && id >= 0) {
                 m.ksc = a.k_scale[(int64_t)id * n_kv + j];
                 m.vsc = a.v_scale[(int64_t)id * n_kv + j];
@@ -354,7 +357,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
 
     // metadata of the consumer's batch (A) and of the next one (Bm)
     Meta A = load_meta(0);
-    Meta Bm = cnt > 64 ? load_meta(1) : Meta{-1, 0, 1.0f, 1.0f};
+    Meta Bm = cnt > 64 ? load_meta(1) : Meta{-1, 0, 0, 1.0f, 1.0f};
     int batchA = 0;
     auto meta_id = [&](int i) {
         const int v = (i >> 6) == batchA ? A.id : Bm.id;
@@ -363,6 +366,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     auto meta_info = [&](int i) {
         const int v = (i >> 6) == batchA ? A.info : Bm.info;
         return __builtin_amdgcn_readlane(v, i & 63);
+    };
+    auto meta_mask = [&](int i) {
+        const int v = (i >> 6) == batchA ? A.mask : Bm.mask;
+        return (uint32_t)__builtin_amdgcn_readlane(v, i & 63);
     };
     auto meta_f = [&](float fa, float fb, int i) {
         const float v = (i >> 6) == batchA ? fa : fb;
@@ -440,7 +447,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             if ((batchA + 1) * 64 < cnt) Bm = load_meta(batchA + 1);
         }
         const int info = meta_info(i);
-        const int valid = info & 31;
+        const uint32_t mask = meta_mask(i);
         const bool seg_first = (info >> 5) & 1;
         const bool seg_last = (info >> 6) & 1;
         const int seg = (int)((unsigned)info >> 8);
@@ -459,12 +466,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             }
         }
         if (meta_id(i) < 0) piece_bad = true;
-        if (valid < 16) {
-            // rows past the sequence's end hold stale data (possibly NaN):
-            // zero them so that 0-weight products stay 0
+        if (mask != 0xFFFFu) {
+            // rows past the sequence's end (or outside the window) may hold
+            // stale data, possibly NaN: zero them so 0-weight products stay 0
 #pragma unroll
             for (int l = 0; l < T::LOADS; ++l)
-                if (vrow[l] >= valid) vr[s][l] = make_uint4(0, 0, 0, 0);
+                if (!((mask >> vrow[l]) & 1u)) vr[s][l] = make_uint4(0, 0, 0, 0);
         }
         // stage V (as bf16) into this wave's LDS tile
 #pragma unroll
@@ -499,7 +506,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             sv[e] = st[e] * mult;
-            if (valid < 16 && 4 * grp + e >= valid) sv[e] = -__builtin_inff();
+            if (!((mask >> (4 * grp + e)) & 1u)) sv[e] = -__builtin_inff();
         }
         const float mx = max_rows4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
         // Lazy rescaling: the reference max of a head moves only when the

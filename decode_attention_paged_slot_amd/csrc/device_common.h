@@ -94,4 +94,43 @@ __device__ __forceinline__ u32x2 int8x4_to_bf16x4(uint32_t w) {
     return r;
 }
 
+// Attended positions of an n-token row: all t < n (window == 0), or with a
+// sliding window t < sinks or t >= n - window. A row lists the logical blocks
+// that hold attended positions: the sink blocks [0, sb) and the window blocks
+// [wstart, nblk); the blocks in between are skipped entirely.
+struct RowBlocks {
+    int count;    // attended blocks of the row
+    int sb;       // leading (sink) blocks
+    int wstart;   // logical block of the first window block
+};
+
+__device__ __forceinline__ RowBlocks row_blocks(int n, int window, int sinks) {
+    const int nblk = (n + 15) >> 4;
+    if (window <= 0 || n <= sinks + window) return RowBlocks{nblk, nblk, nblk};
+    const int sb = (sinks + 15) >> 4;
+    const int wstart = max((n - window) >> 4, sb);
+    return RowBlocks{sb + (nblk - wstart), sb, wstart};
+}
+
+// The i-th attended block of a row -> its logical block.
+__device__ __forceinline__ int row_block_logical(const RowBlocks& r, int i) {
+    return i < r.sb ? i : r.wstart + (i - r.sb);
+}
+
+// Bit k set <=> position 16 L + k of the row is attended.
+__device__ __forceinline__ uint32_t block_token_mask(int L, int n, int window, int sinks) {
+    const int t0 = 16 * L;
+    uint32_t m = n - t0 >= 16 ? 0xFFFFu : (n > t0 ? (1u << (n - t0)) - 1u : 0u);
+    if (window > 0) {
+        uint32_t keep = 0;
+        const int s = sinks - t0;             // positions below it are sinks
+        if (s > 0) keep |= s >= 16 ? 0xFFFFu : (1u << s) - 1u;
+        const int w0 = n - window - t0;       // first window position in the block
+        if (w0 <= 0) keep = 0xFFFFu;
+        else if (w0 < 16) keep |= 0xFFFFu & ~((1u << w0) - 1u);
+        m &= keep;
+    }
+    return m;
+}
+
 }  // namespace pda

@@ -64,6 +64,7 @@ struct AttnArgs {
     int32_t P, bpp;
     int32_t nw, split;
     int32_t reuse_blocks;   // leading logical blocks read with cache-retaining loads
+    int32_t window, sinks;  // sliding window (0 = all positions) and its sink tokens
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s);

@@ -202,6 +202,11 @@ typedef struct pda_attn_desc {
                                     served from L2 / Infinity Cache after their first read);
                                     all other blocks are streamed with non-temporal loads.
                                     0 = stream everything. Affects speed only, never results. */
+    int32_t window;             /* sliding window: > 0 attends only to the last `window`
+                                   positions of each row, plus its first sink_tokens
+                                   positions; 0 = every position  ["9 Decode and KV Cache",
+                                   section 9.7; sink and sliding-window teasers] */
+    int32_t sink_tokens;        /* attention sinks kept with a window (ignored if window == 0) */
     int32_t reserved;           /* must be 0 */
 } pda_attn_desc;
 
@@ -221,7 +226,10 @@ int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
 /* Paged decode attention  [sections 9.4-9.5; SoK paper section 1.1]: for
  * every row b and query head h, with j = h / g and n = context_lens[b],
  *   s_t   = scale * <q[b][h], K[pb(t)][j][t % bs]>,  pb(t) = block_table[b][t / bs]
- *   out[b][h] = sum_{t < n} softmax(s)_t * V[pb(t)][j][t % bs]
+ *   out[b][h] = sum_{t in A} softmax(s)_t * V[pb(t)][j][t % bs]
+ * over the attended positions A = { t < n } (window == 0), or with a sliding
+ * window A = { t < n : t < sink_tokens or t >= n - window } (section 9.7);
+ * positions outside A are never looked up or read.
  * evaluated in fp32 with exact-product matrix-core accumulation; the cache is
  * read once per step and no score is written to memory (SoK appendices A.1,
  * C.4). Long contexts are split into partitions whose partial results are

@@ -59,6 +59,8 @@ class Workload:
     sink_factor: float = 1.0           # ... are multiplied by this (exact in bf16)
     shared_prefix_tokens: int = 0      # first tokens' blocks shared by all rows
     scale: Optional[float] = None      # softmax scale; None -> 1/sqrt(d_h)
+    attn_window: int = 0               # sliding window of the attention call (0 = none)
+    attn_sinks: int = 0                # attention-sink tokens kept with the window
 
     @property
     def g(self) -> int:
@@ -88,9 +90,13 @@ QUANT_PREFIX_FP8 = Workload("quant_prefix_fp8", 5, B=64, n_q=32, n_kv=8, d_h=128
                             block_size=16, kv_dtype=FP8, q_dtype=BF16, ctx_lo=1024,
                             ctx_hi=16384, shared_prefix_tokens=2048)
 QUANT_PREFIX_INT8 = QUANT_PREFIX_FP8.with_(name="quant_prefix_int8", seed=6, kv_dtype=INT8)
+# the 70B layer with a Mistral-style 4096-token sliding window plus the first
+# 4 tokens kept as attention sinks ("9 Decode and KV Cache", section 9.7)
+LLAMA70B_WINDOW = LLAMA70B_LAYER.with_(name="llama3_70b_layer_b8_32k_window4k_sinks4", seed=7,
+                                       attn_window=4096, attn_sinks=4)
 
 WORKLOADS = {w.name: w for w in (TINY_MHA, LLAMA8B_LAYER, LLAMA70B_LAYER, LONG_SINKS,
-                                 QUANT_PREFIX_FP8, QUANT_PREFIX_INT8)}
+                                 QUANT_PREFIX_FP8, QUANT_PREFIX_INT8, LLAMA70B_WINDOW)}
 
 
 # ---------------------------------------------------------------- primitives

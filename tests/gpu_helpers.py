@@ -25,7 +25,7 @@ def to_dev(a: np.ndarray, code: int, dev):
 
 
 def run_case(case, *, out_dtype=F32, num_partitions=0, max_context=None, total_context=0,
-             table=None, reuse_prefix_blocks=0, dev="cuda"):
+             table=None, reuse_prefix_blocks=0, window=0, sinks=0, dev="cuda"):
     """Paged decode attention of a tests.helpers.Case on the GPU -> fp32 numpy
     [B, n_q, d_h] (or the raw bf16 tensor's fp32 values for out_dtype=BF16)."""
     import torch
@@ -40,7 +40,7 @@ def run_case(case, *, out_dtype=F32, num_partitions=0, max_context=None, total_c
     mc = int(case.ctx.max()) if (max_context is None and case.B) else (max_context or 0)
     desc = pda.AttnDesc(case.B, case.n_q, case.n_kv, case.d_h, case.bs, bt.shape[1],
                         k.shape[0], case.kv_dtype, case.q_dtype, out_dtype, mc,
-                        num_partitions, total_context, reuse_prefix_blocks, 0)
+                        num_partitions, total_context, reuse_prefix_blocks, window, sinks, 0)
     ws = pda.workspace_for(desc, dev)
     if case.kv_dtype in (FP8, INT8):
         ks = torch.from_numpy(case.k_scale).to(dev)

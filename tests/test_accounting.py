@@ -86,3 +86,17 @@ def test_step_bytes_shared_prefix_unique():
     # rows share min(128, blocks-1) blocks: 128, 127, 6 -> duplicates 127 + 6 blocks
     dup = (127 + 6) * 16 * 8 * 128 * 2
     assert sb.kv_read - sb.kv_read_unique == dup
+
+
+def test_window_accounting():
+    """A 4096-token window with 4 sinks on a 32k row reads 4100 positions in
+    257 + 1 blocks; short rows are read whole."""
+    assert acc.attended_tokens(32768, 4096, 4) == 4100
+    assert acc.attended_blocks(32768, 16, 4096, 4) == 1 + 256
+    assert acc.attended_tokens(4000, 4096, 4) == 4000
+    assert acc.attended_blocks(4000, 16, 4096, 4) == 250
+    # window start in the middle of a block: that block counts once
+    assert acc.attended_blocks(100, 16, 30, 0) == 3      # positions 70..99 -> blocks 4, 5, 6
+    # sinks and window sharing a block
+    assert acc.attended_blocks(40, 16, 20, 5) == 3       # 0..4 -> block 0; 20..39 -> blocks 1, 2
+    assert acc.attended_blocks(40, 16, 30, 5) == 3       # 0..4 and 10..39 share block 0

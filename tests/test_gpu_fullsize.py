@@ -24,7 +24,7 @@ from tests.gpu_helpers import TOL_16BIT, TOL_8BIT
 pytestmark = pytest.mark.gpu
 
 FULL = ["tiny_mha", "llama3_8b_layer", "llama3_70b_layer_b8_32k", "long_context_131k_sinks",
-        "quant_prefix_fp8", "quant_prefix_int8"]
+        "quant_prefix_fp8", "quant_prefix_int8", "llama3_70b_layer_b8_32k_window4k_sinks4"]
 
 
 def _raw(t):
@@ -84,7 +84,8 @@ def test_full_size_workload(name):
     out = torch.full((w.B, w.n_q, w.d_h), float("nan"), device=dev)
     desc = pda.attn_desc(inp.q, inp.k_cache, bt, max_context=int(inp.ctx.max()),
                          kv_dtype=w.kv_dtype, total_context=int(inp.ctx.sum()),
-                         reuse_prefix_blocks=w.shared_prefix_tokens // w.block_size)
+                         reuse_prefix_blocks=w.shared_prefix_tokens // w.block_size,
+                         window=w.attn_window, sink_tokens=w.attn_sinks)
     ws = pda.workspace_for(desc, dev)
     if quant:
         pda.kv_append_quant(inp.k_new, inp.v_new, sl, inp.k_cache, inp.v_cache, inp.k_scale,
@@ -116,7 +117,8 @@ def test_full_size_workload(name):
     rows = _sample_rows(w, np.random.default_rng(w.seed + 100))
     ref, _, _, bad = oracle.paged_attn(q_h, k2, v2, table, inp.ctx, w.softmax_scale, n_q=w.n_q,
                                        n_kv=w.n_kv, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                                       k_scale=ks_h, v_scale=vs_h, rows=rows)
+                                       k_scale=ks_h, v_scale=vs_h, rows=rows,
+                                       window=w.attn_window, sinks=w.attn_sinks)
     assert bad == 0
     got = out.reshape(w.B * w.n_q, w.d_h)[torch.from_numpy(rows).to(dev)].cpu().numpy()
     assert np.isfinite(got).all()

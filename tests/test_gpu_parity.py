@@ -81,6 +81,39 @@ def test_stream_default_plan_many_short_rows(d_h, g):
     assert max_err(got2, c.oracle_out()) < TOL_16BIT
 
 
+WINDOWS = [(1, 0), (20, 4), (33, 17), (100, 0), (5, 40), (4096, 4)]
+
+
+@pytest.mark.parametrize("kv_dtype", [BF16, FP8, F32])
+@pytest.mark.parametrize("window,sinks", WINDOWS)
+@pytest.mark.parametrize("nw", [0, 1, 7])
+def test_window_with_sinks(kv_dtype, window, sinks, nw):
+    """Sliding window with attention sinks: positions outside it are NaN-
+    poisoned and one block holding only such positions is unmapped; neither
+    may reach the output."""
+    import synth
+    ctx = [0, 700, 1, 33, 2000, 16, 300]
+    c = make_case(2700 + window + sinks + kv_dtype, ctx, n_q=8, n_kv=2, d_h=128,
+                  kv_dtype=kv_dtype, q_dtype=BF16 if kv_dtype != F32 else F32)
+    nan = {F32: np.float32(np.nan), BF16: synth.BF16_NAN, FP8: synth.FP8_NAN}[kv_dtype]
+    table = c.table.copy()
+    for b, n in enumerate(c.ctx):
+        for t in range(n):
+            if not (t < sinks or t >= n - window):
+                pb = table[b, t // 16]
+                c.k[pb, :, t % 16, :] = nan
+                c.v[pb, :, t % 16, :] = nan
+        # unmap the blocks that hold no attended position (never looked up)
+        for blk in range((n + 15) // 16):
+            if all(not (t < sinks or t >= n - window) for t in range(16 * blk, min(n, 16 * blk + 16))):
+                table[b, blk] = -1
+    _say(f"window={window} sinks={sinks} kv={kv_dtype} nw={nw}")
+    got, _ = run_case(c, table=table, window=window, sinks=sinks, num_partitions=nw)
+    ref = c.oracle_out(window=window, sinks=sinks)
+    assert (got[0] == 0).all()
+    assert max_err(got, ref) < (TOL_8BIT if kv_dtype == FP8 else TOL_16BIT)
+
+
 def test_fp32_query_with_bf16_cache():
     c = make_case(3001, CTX_RAGGED, n_q=8, n_kv=2, d_h=128, q_dtype=F32)
     _say("fp32 q, bf16 cache")
