@@ -4,7 +4,9 @@
 One step = one decode step of one attention layer over a whole batch: the
 step's new K/V rows are appended into their mapped cache slots, then every
 sequence's query attends over its paged cache (split-KV partitions and their
-log-sum-exp merge included). Inputs are seeded synthetic tensors drawn in HBM
+log-sum-exp merge included). By default the step is one fused
+pda_decode_step launch (plus the merge); --two-calls runs pda_kv_append then
+pda_paged_decode_attn, with bit-identical results. Inputs are seeded synthetic tensors drawn in HBM
 before the timed region; nothing is copied between host and device inside it.
 
 Default workload: the Llama-3-70B layer shape on one GPU -- batch 8, 64 query
@@ -61,6 +63,9 @@ def parse_args(argv=None):
     ap.add_argument("--no-probe", action="store_true", help="skip the stream-copy probe")
     ap.add_argument("--num-partitions", type=int, default=0,
                     help="split-KV partitions (0 = the library's choice)")
+    ap.add_argument("--two-calls", dest="fused", action="store_false", default=True,
+                    help="pda_kv_append + pda_paged_decode_attn per step instead of one fused "
+                         "pda_decode_step launch (the default; identical results)")
     ap.add_argument("--graph", dest="graph", action="store_true", default=False,
                     help="replay the step from a captured HIP graph (eager launches by "
                          "default: on this stack a replay adds ~6 us per step)")
@@ -253,9 +258,22 @@ def main(argv=None) -> int:
             pda.paged_decode_attn(inp.q, inp.k_cache, inp.v_cache, bt, cl, scale, out,
                                   desc=desc, workspace=ws)
 
-    def step():
-        append()
-        attend()
+    if args.fused:
+        desc.new_dtype = synth.BF16 if w.kv_dtype != synth.F32 else synth.F32
+
+        def step():
+            # one launch: each row's new K/V land at position n - 1, then attention
+            if quant:
+                pda.decode_step_quant(inp.q, inp.k_new, inp.v_new, inp.k_cache, inp.v_cache,
+                                      inp.k_scale, inp.v_scale, bt, cl, scale, out, desc=desc,
+                                      workspace=ws)
+            else:
+                pda.decode_step(inp.q, inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, bt, cl,
+                                scale, out, desc=desc, workspace=ws)
+    else:
+        def step():
+            append()
+            attend()
 
     # Clock settle (untimed): MI355X takes ~15-20 ms of sustained work to
     # reach its steady clocks; the first steps of a cold GPU run up to 1.5x
@@ -388,7 +406,8 @@ def main(argv=None) -> int:
                         "attention_avg": round(att_avg * 1e3, 2),
                         "attention_avg_min": round(min(att_ms) * 1e3, 2),
                         "attention_avg_max": round(max(att_ms) * 1e3, 2)},
-        "timing": ("graph replay of the step" if graph is not None else "eager launches") +
+        "timing": ("fused decode step; " if args.fused else "") +
+                  ("graph replay of the step" if graph is not None else "eager launches") +
                   "; per-call averages from back-to-back calls between two HIP events",
         "bytes_per_step": {"attention": sb.attention, "attention_unique": sb.attention_unique,
                            "step": sb.step, "kv_read": sb.kv_read},

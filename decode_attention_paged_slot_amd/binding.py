@@ -61,7 +61,7 @@ class AttnDesc(ctypes.Structure):
                 ("out_dtype", ctypes.c_int32), ("max_context", ctypes.c_int32),
                 ("num_partitions", ctypes.c_int32), ("total_context", ctypes.c_int64),
                 ("reuse_prefix_blocks", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("sink_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("sink_tokens", ctypes.c_int32), ("new_dtype", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -87,6 +87,10 @@ _SIGS = {
     "pda_paged_decode_attn_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                            _vp, ctypes.POINTER(AttnDesc), _vp, _sz, _vp]),
     "pda_lse_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "pda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                               ctypes.POINTER(AttnDesc), _vp, _sz, _vp]),
+    "pda_decode_step_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                     _vp, ctypes.POINTER(AttnDesc), _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -166,14 +170,15 @@ def kv_append_quant(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_sca
 def attn_desc(q, k_cache, block_table, *, max_context: int, out_dtype: int = F32,
               kv_dtype: Optional[int] = None, num_partitions: int = 0,
               total_context: int = 0, reuse_prefix_blocks: int = 0, window: int = 0,
-              sink_tokens: int = 0) -> AttnDesc:
+              sink_tokens: int = 0, new_dtype: Optional[int] = None) -> AttnDesc:
     B, n_q, d_h = q.shape
     nb, n_kv, bs, d2 = k_cache.shape
     assert d2 == d_h
     kvd = kv_dtype if kv_dtype is not None else dtype_code(k_cache)
     return AttnDesc(B, n_q, n_kv, d_h, bs, int(block_table.shape[1]), nb, kvd, dtype_code(q),
                     out_dtype, int(max_context), int(num_partitions), int(total_context),
-                    int(reuse_prefix_blocks), int(window), int(sink_tokens), 0)
+                    int(reuse_prefix_blocks), int(window), int(sink_tokens),
+                    kvd if new_dtype is None else int(new_dtype))
 
 
 def attn_workspace_size(desc: AttnDesc) -> int:
@@ -241,6 +246,34 @@ def paged_decode_attn_quant(q, k_cache, v_cache, k_scale, v_scale, block_table, 
                                             float(scale), _ptr(out), ctypes.byref(desc),
                                             _ptr(workspace), ws_bytes, _stream(stream)),
            "pda_paged_decode_attn_quant")
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, block_table, context_lens, scale: float,
+                out, *, desc: AttnDesc, workspace=None, stream=None) -> None:
+    """pda_decode_step: append each row's new K/V at position n - 1 and
+    attend, in one launch (f32 / bf16 caches; k_new, v_new [B, n_kv, d_h])."""
+    if workspace is None:
+        workspace = workspace_for(desc, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pda_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_table), _ptr(context_lens), float(scale), _ptr(out),
+                                ctypes.byref(desc), _ptr(workspace), ws_bytes, _stream(stream)),
+           "pda_decode_step")
+
+
+def decode_step_quant(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                      context_lens, scale: float, out, *, desc: AttnDesc, workspace=None,
+                      stream=None) -> None:
+    """pda_decode_step_quant: as decode_step on an 8-bit cache; the new rows
+    (desc.new_dtype f32 / bf16) are encoded with their blocks' scales."""
+    if workspace is None:
+        workspace = workspace_for(desc, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pda_decode_step_quant(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                      _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                      _ptr(block_table), _ptr(context_lens), float(scale),
+                                      _ptr(out), ctypes.byref(desc), _ptr(workspace), ws_bytes,
+                                      _stream(stream)), "pda_decode_step_quant")
 
 
 def lse_merge(part_o, part_ml, out, *, stream=None) -> None:

@@ -172,7 +172,7 @@ int32_t check_attn_desc(const pda_attn_desc* d, bool quant) {
     }
     if (d->max_blocks_per_seq <= 0 || d->num_blocks <= 0 || d->max_context < 0 ||
         d->num_partitions < 0 || d->total_context < 0 || d->reuse_prefix_blocks < 0 ||
-        d->window < 0 || d->sink_tokens < 0 || d->reserved != 0) {
+        d->window < 0 || d->sink_tokens < 0) {
         set_error("bad sizes: max_blocks_per_seq=%d num_blocks=%d max_context=%d",
                   d->max_blocks_per_seq, d->num_blocks, d->max_context);
         return PDA_EINVAL;
@@ -235,10 +235,23 @@ int32_t debug_check(const pda_attn_desc* d, const int32_t* block_table,
 int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
                  const float* v_scale, const int32_t* block_table, const int32_t* context_lens,
                  float scale, void* out, const pda_attn_desc* d, void* workspace,
-                 size_t ws_bytes, void* stream, bool quant) {
+                 size_t ws_bytes, void* stream, bool quant, const void* k_new = nullptr,
+                 const void* v_new = nullptr, bool fused = false) {
     int32_t rc = check_attn_desc(d, quant);
     if (rc != PDA_OK) return rc;
+    if (fused) {
+        const bool ok = quant ? (d->new_dtype == PDA_F32 || d->new_dtype == PDA_BF16)
+                              : d->new_dtype == d->kv_dtype;
+        if (!ok) {
+            set_error("new_dtype %d does not fit the cache dtype %d", d->new_dtype, d->kv_dtype);
+            return PDA_EINVAL;
+        }
+    }
     if (d->B == 0) return PDA_OK;
+    if (fused && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) {
+        set_error("k_new / v_new must be 16-byte aligned device pointers");
+        return PDA_EINVAL;
+    }
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
         (quant && (!k_scale || !v_scale))) {
         set_error("NULL device pointer");
@@ -293,6 +306,9 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     a.reuse_blocks = d->reuse_prefix_blocks;
     a.window = d->window;
     a.sinks = d->window > 0 ? d->sink_tokens : 0;
+    a.k_new = fused ? k_new : nullptr;
+    a.v_new = fused ? v_new : nullptr;
+    a.new_dtype = d->new_dtype;
     hipError_t e;
     if (plan.stream) {
         e = launch_attn_mfma(a, s);
@@ -431,6 +447,24 @@ int32_t pda_paged_decode_attn_quant(const void* q, const void* k_cache, const vo
                                     void* workspace, size_t ws_bytes, void* stream) {
     return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
                     d, workspace, ws_bytes, stream, true);
+}
+
+int32_t pda_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                        void* v_cache, const int32_t* block_table, const int32_t* context_lens,
+                        float scale, void* out, const pda_attn_desc* d, void* workspace,
+                        size_t ws_bytes, void* stream) {
+    return run_attn(q, k_cache, v_cache, nullptr, nullptr, block_table, context_lens, scale, out,
+                    d, workspace, ws_bytes, stream, false, k_new, v_new, true);
+}
+
+int32_t pda_decode_step_quant(const void* q, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, const float* k_scale,
+                              const float* v_scale, const int32_t* block_table,
+                              const int32_t* context_lens, float scale, void* out,
+                              const pda_attn_desc* d, void* workspace, size_t ws_bytes,
+                              void* stream) {
+    return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
+                    d, workspace, ws_bytes, stream, true, k_new, v_new, true);
 }
 
 int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,

@@ -81,11 +81,23 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_f32(AttnArgs a) {
         const bool live = (bm >> t) & 1u;
         const float* kt = (const float*)a.k + ((int64_t)pb * a.n_kv + j) * tile + t * HD;
         const float* vt = (const float*)a.v + ((int64_t)pb * a.n_kv + j) * tile + t * HD;
+        // fused decode step: position n - 1 takes the new token's K/V (all
+        // query heads of the group use it; the group's first head writes it)
+        const bool fresh = a.k_new != nullptr && 16 * kb + t == n - 1;
+        const float* kn = (const float*)a.k_new + ((int64_t)b * a.n_kv + j) * HD;
+        const float* vn = (const float*)a.v_new + ((int64_t)b * a.n_kv + j) * HD;
         float kv[NV][4], vv[NV][4];
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             float4 x = make_float4(0, 0, 0, 0), y = make_float4(0, 0, 0, 0);
-            if (live) {
+            if (fresh) {
+                x = *(const float4*)(kn + 4 * (part + 4 * k));
+                y = *(const float4*)(vn + 4 * (part + 4 * k));
+                if (h % a.g == 0) {
+                    *(float4*)(kt + 4 * (part + 4 * k)) = x;
+                    *(float4*)(vt + 4 * (part + 4 * k)) = y;
+                }
+            } else if (live) {
                 x = *(const float4*)(kt + 4 * (part + 4 * k));
                 y = *(const float4*)(vt + 4 * (part + 4 * k));
             }

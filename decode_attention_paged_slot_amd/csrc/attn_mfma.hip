@@ -136,6 +136,45 @@ __device__ __forceinline__ bf16x8 kv_operand_from_bytes(uint4 w, int half) {
 }
 
 
+// 16 new-row elements (fp32 or bf16 at `src`) -> 16 cache codes, encoded with
+// the destination block's reciprocal scale exactly as the quantized append
+// encodes them: y = x * fp32(1 / scale), round to nearest even, saturate.
+template <int KV>
+__device__ __forceinline__ uint4 encode16(const char* src, int src_dtype, float inv) {
+    float x[16];
+    if (src_dtype == DT_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 f = *(const float4*)(src + 16 * i);
+            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint4 w = *(const uint4*)(src + 16 * i);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[8 * i + 2 * k] = bf16_lo_to_f32(ws[k]);
+                x[8 * i + 2 * k + 1] = bf16_hi_to_f32(ws[k]);
+            }
+        }
+    }
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float y = __fmul_rn(x[4 * k + e], inv);
+            const uint32_t code = KV == DT_FP8 ? quant_fp8_e4m3(y) : ((uint32_t)quant_int8(y) & 0xFFu);
+            w |= code << (8 * e);
+        }
+        packed[k] = w;
+    }
+    return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
 // Per-block metadata, lane i of a 64-block batch describing block i.
 //   info bit 5 first block of its segment, bit 6 last block of its
 //   segment, bit 7 shared (cache-retaining loads), bits 8.. segment index.
@@ -376,6 +415,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i & 63));
     };
 
+    auto ksc_of = [&](int i) { return QUANT ? meta_f(A.ksc, Bm.ksc, i) : 1.0f; };
+    auto vsc_of = [&](int i) { return QUANT ? meta_f(A.vsc, Bm.vsc, i) : 1.0f; };
+
     uint4 kr[kDepth][T::LOADS], vr[kDepth][T::LOADS];
 
     // Loads are never predicated (a partially filled final block is still a
@@ -465,7 +507,48 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
                 a.seg_info[seg] = make_int2(wg, last_wave);
             }
         }
-        if (meta_id(i) < 0) piece_bad = true;
+        const int pb_i = meta_id(i);
+        // block scales, read while every lane is active (a readlane inside a
+        // divergent branch would read an unselected lane's stale register)
+        const float ksc = ksc_of(i);
+        const float vsc = vsc_of(i);
+        if (pb_i < 0) piece_bad = true;
+        if (a.k_new != nullptr && seg_last && pb_i >= 0) {
+            // fused decode step: this block holds the row's newest position
+            // n - 1; its K/V rows come from the new token (replacing what
+            // the tile load brought) and are written to the cache slot
+            const int b = seg / n_kv, j = seg - (seg / n_kv) * n_kv;
+            const int r = (nn[b] - 1) & 15;
+            char* kt = (char*)kbase + (int64_t)pb_i * block_stride + (int64_t)j * head_stride;
+            char* vt = (char*)vbase + (int64_t)pb_i * block_stride + (int64_t)j * head_stride;
+            const int src_w = a.new_dtype == DT_F32 ? 4 : 2;   // bytes per new-row element
+            const char* knew = (const char*)a.k_new + (int64_t)seg * HD * src_w;
+            const char* vnew = (const char*)a.v_new + (int64_t)seg * HD * src_w;
+            if (col == r) {
+#pragma unroll
+                for (int l = 0; l < T::LOADS; ++l) {
+                    const int e0 = (64 * l + 16 * grp) / T::W;   // first element of the chunk
+                    uint4 w;
+                    if constexpr (KV == DT_BF16) w = ld16(knew + 2 * e0);
+                    else w = encode16<KV>(knew + (int64_t)src_w * e0, a.new_dtype,
+                                          __fdiv_rn(1.0f, ksc));
+                    kr[s][l] = w;
+                    *(uint4*)(kt + r * T::ROWB + 64 * l + 16 * grp) = w;
+                }
+            }
+#pragma unroll
+            for (int l = 0; l < T::LOADS; ++l) {
+                if (vrow[l] == r) {
+                    const int e0 = ((1024 * l + 16 * lane) - r * T::ROWB) / T::W;
+                    uint4 w;
+                    if constexpr (KV == DT_BF16) w = ld16(vnew + 2 * e0);
+                    else w = encode16<KV>(vnew + (int64_t)src_w * e0, a.new_dtype,
+                                          __fdiv_rn(1.0f, vsc));
+                    vr[s][l] = w;
+                    *(uint4*)(vt + 1024 * l + 16 * lane) = w;
+                }
+            }
+        }
         if (mask != 0xFFFFu) {
             // rows past the sequence's end (or outside the window) may hold
             // stale data, possibly NaN: zero them so 0-weight products stay 0
@@ -495,8 +578,6 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[c], st, 0, 0, 0);
             if (QT == DT_F32) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
         }
-        const float ksc = QUANT ? meta_f(A.ksc, Bm.ksc, i) : 1.0f;
-        const float vsc = QUANT ? meta_f(A.vsc, Bm.vsc, i) : 1.0f;
         // refill this slot with the block kDepth ahead
         if (refill) issue(s, i + kDepth);
 

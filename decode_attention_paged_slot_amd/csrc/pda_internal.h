@@ -65,6 +65,11 @@ struct AttnArgs {
     int32_t nw, split;
     int32_t reuse_blocks;   // leading logical blocks read with cache-retaining loads
     int32_t window, sinks;  // sliding window (0 = all positions) and its sink tokens
+    // fused decode step: the new rows [B][n_kv][d_h] of new_dtype, written into
+    // position n - 1 of each row (nullptr: attention only)
+    const void* k_new;
+    const void* v_new;
+    int32_t new_dtype;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s);

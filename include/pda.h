@@ -207,7 +207,8 @@ typedef struct pda_attn_desc {
                                    positions; 0 = every position  ["9 Decode and KV Cache",
                                    section 9.7; sink and sliding-window teasers] */
     int32_t sink_tokens;        /* attention sinks kept with a window (ignored if window == 0) */
-    int32_t reserved;           /* must be 0 */
+    int32_t new_dtype;          /* pda_decode_step*: pda_dtype of k_new / v_new (PDA_F32 or
+                                   PDA_BF16; equal to kv_dtype for 16/32-bit caches) */
 } pda_attn_desc;
 
 /* Workspace bytes pda_paged_decode_attn needs for this descriptor (0 when it
@@ -264,6 +265,36 @@ int32_t pda_paged_decode_attn_quant(const void* q, const void* k_cache, const vo
                                     const int32_t* block_table, const int32_t* context_lens,
                                     float scale, void* out, const pda_attn_desc* d,
                                     void* workspace, size_t ws_bytes, void* stream);
+
+/* One fused decode step: the append of each row's new token followed by
+ * paged decode attention, in one launch  [section 9.4: append path and read
+ * path of the same step]. For every row b with n = context_lens[b] > 0 and
+ * every KV head j, position n - 1 of the row (slot
+ * block_table[b][(n-1)/bs] * bs + (n-1) % bs, as the block-table builder
+ * maps it) receives k_new[b][j][:] / v_new[b][j][:], and the attention of
+ * row b then includes it. The result, in `out` and in the caches, is bit for
+ * bit that of pda_kv_append (slot_mapping as above) followed by
+ * pda_paged_decode_attn; rows with n == 0 or an invalid n append nothing.
+ *   k_new, v_new  device [B][n_kv][d_h], d->new_dtype (== kv_dtype here)
+ *   k_cache, v_cache device caches, read and written
+ * The block receiving a row's new token must not appear in another row's
+ * table (copy on write), as the builder guarantees. Other arguments, errors
+ * and the workspace as for pda_paged_decode_attn. */
+int32_t pda_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                        void* v_cache, const int32_t* block_table, const int32_t* context_lens,
+                        float scale, void* out, const pda_attn_desc* d, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/* Fused decode step on an 8-bit cache: the new rows (d->new_dtype F32 or
+ * BF16) are encoded with their destination block's scales exactly as
+ * pda_kv_append_quant encodes them, then attended as in
+ * pda_paged_decode_attn_quant. */
+int32_t pda_decode_step_quant(const void* q, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, const float* k_scale,
+                              const float* v_scale, const int32_t* block_table,
+                              const int32_t* context_lens, float scale, void* out,
+                              const pda_attn_desc* d, void* workspace, size_t ws_bytes,
+                              void* stream);
 
 /* Log-sum-exp merge of split-KV partial results. For each of `rows` rows and
  * P partials with (o_p, m_p, l_p):

@@ -40,7 +40,8 @@ def run_case(case, *, out_dtype=F32, num_partitions=0, max_context=None, total_c
     mc = int(case.ctx.max()) if (max_context is None and case.B) else (max_context or 0)
     desc = pda.AttnDesc(case.B, case.n_q, case.n_kv, case.d_h, case.bs, bt.shape[1],
                         k.shape[0], case.kv_dtype, case.q_dtype, out_dtype, mc,
-                        num_partitions, total_context, reuse_prefix_blocks, window, sinks, 0)
+                        num_partitions, total_context, reuse_prefix_blocks, window, sinks,
+                        case.kv_dtype)
     ws = pda.workspace_for(desc, dev)
     if case.kv_dtype in (FP8, INT8):
         ks = torch.from_numpy(case.k_scale).to(dev)

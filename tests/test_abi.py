@@ -49,7 +49,7 @@ def _desc(**kw):
     base = dict(B=2, n_q=8, n_kv=2, d_h=128, block_size=16, max_blocks_per_seq=64,
                 num_blocks=200, kv_dtype=pda.BF16, q_dtype=pda.BF16, out_dtype=pda.F32,
                 max_context=1000, num_partitions=0, total_context=0, reuse_prefix_blocks=0,
-                window=0, sink_tokens=0, reserved=0)
+                window=0, sink_tokens=0, new_dtype=pda.BF16)
     base.update(kw)
     return pda.AttnDesc(*[base[f] for f, _ in pda.AttnDesc._fields_])
 
@@ -59,7 +59,7 @@ def _desc(**kw):
                                  dict(q_dtype=pda.INT8), dict(out_dtype=pda.FP8_E4M3),
                                  dict(max_blocks_per_seq=0), dict(num_blocks=0),
                                  dict(max_context=-1), dict(B=-1),
-                                 dict(reuse_prefix_blocks=-1), dict(reserved=1),
+                                 dict(reuse_prefix_blocks=-1),
                                  dict(window=-1), dict(sink_tokens=-1)])
 def test_attention_descriptor_validation(bad):
     with pytest.raises(pda.PdaError):
