@@ -67,7 +67,14 @@ struct Tr {
     static constexpr int LTILE = 16 * LROW;
     static constexpr int CPR = HD / 8;                  // 16-B chunks per LDS row
     static constexpr int RPS = 256 / LROW;              // LDS rows per 256 B
+    static constexpr int CPRB = ROWB / 16;              // 16-B chunks per cache row
 };
+
+// XOR swizzle of the bf16 K staging tile (16 rows of 2 * HD bytes).
+template <int HD>
+__device__ __forceinline__ constexpr int kswz(int r) {
+    return HD == 128 ? (r & 15) : ((r >> 1) & 7);
+}
 
 // First element of QK chunk c held by lane group grp (8 consecutive elements).
 template <int HD, int KV>
@@ -191,7 +198,9 @@ template <int HD, int KV, int QT>
 __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     using T = Tr<HD, KV>;
     constexpr bool QUANT = KV != DT_BF16;
-    __shared__ __attribute__((aligned(16))) char stage_all[4 * T::LTILE];
+    // per wave: the V tile (bf16) and, for bf16 caches, the K tile
+    constexpr bool KST = KV == DT_BF16;
+    __shared__ __attribute__((aligned(16))) char stage_all[4 * T::LTILE * (KST ? 2 : 1)];
     __shared__ int wsum[4];
     extern __shared__ int dyn_lds[];
     int* pre = dyn_lds;             // [B + 1] exclusive prefix of blocks per sequence
@@ -372,6 +381,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     int q_seg = -1;
 
     char* stage = stage_all + wave * T::LTILE;
+    char* kstage = stage_all + (4 + wave) * T::LTILE;   // used when KST
     const char* kbase = (const char*)a.k;
     const char* vbase = (const char*)a.v;
     const int64_t head_stride = T::TILEB;
@@ -385,13 +395,21 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
         vrow[l] = byte / T::ROWB;
         vcb[l] = ((byte % T::ROWB) / T::W) / 8;   // bf16 chunk of the first element
     }
-    // transposed-read addresses for the value operand: lane L reads row L/4,
-    // columns 16 n + 4 (L % 4) .. +3
-    int trd[T::NT];
+    // Transposed-read addresses for the value operand of the packed product
+    // O^T += [V^T | V^T] . [P_hi ; P_lo] (MFMA 16x16x32, K = 32 = the block's
+    // 16 tokens twice): lane l must hold V^T[d = 16 t + l % 16][tokens
+    // base + 0..7] with base = 0 for lane rows 0 and 2, 8 for rows 1 and 3.
+    // ds_read_b64_tr_b16 hands each 16-lane row G the 4 panel rows its own
+    // lanes address (lane L: token of panel row L / 4, columns
+    // 16 t + 4 (L % 4) .. +3), so two reads (tokens base + 0..3, base + 4..7)
+    // give the 8 tokens.
+    int trd0[T::NT], trd1[T::NT];
 #pragma unroll
     for (int t = 0; t < T::NT; ++t) {
-        const int r = lane >> 2, q4 = lane & 3;
-        trd[t] = lds_off<HD>(r, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
+        const int base = (grp & 1) * 8, q4 = lane & 3;
+        const int r0 = base + ((lane & 15) >> 2);
+        trd0[t] = lds_off<HD>(r0, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
+        trd1[t] = lds_off<HD>(r0 + 4, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
     }
 
     // metadata of the consumer's batch (A) and of the next one (Bm)
@@ -432,15 +450,19 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
         const int j = (int)((unsigned)info >> 8) % n_kv;
         const char* kt = kbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
         const char* vt = vbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
+        // bf16 K: contiguous 1 KiB per load instruction (staged through LDS
+        // into the operand layout); 8-bit K: straight into the operand
+        // registers, lane (t, grp) taking 16 B of token row t
+        const int koff = KST ? 16 * lane : col * T::ROWB + 16 * grp;
+        const int kstep = KST ? 1024 : 64;
         if ((info >> 7) & 1) {
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16(kt + col * T::ROWB + 64 * l + 16 * grp);
+            for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16(kt + koff + kstep * l);
 #pragma unroll
             for (int l = 0; l < T::LOADS; ++l) vr[s][l] = ld16(vt + 1024 * l + 16 * lane);
         } else {
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l)
-                kr[s][l] = ld16_stream(kt + col * T::ROWB + 64 * l + 16 * grp);
+            for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16_stream(kt + koff + kstep * l);
 #pragma unroll
             for (int l = 0; l < T::LOADS; ++l) vr[s][l] = ld16_stream(vt + 1024 * l + 16 * lane);
         }
@@ -524,14 +546,22 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             const int src_w = a.new_dtype == DT_F32 ? 4 : 2;   // bytes per new-row element
             const char* knew = (const char*)a.k_new + (int64_t)seg * HD * src_w;
             const char* vnew = (const char*)a.v_new + (int64_t)seg * HD * src_w;
-            if (col == r) {
+            if constexpr (KST) {
+#pragma unroll
+                for (int l = 0; l < T::LOADS; ++l) {
+                    if (vrow[l] == r) {   // contiguous K: same lanes as V
+                        const int b0 = (1024 * l + 16 * lane) - r * T::ROWB;
+                        const uint4 w = ld16(knew + b0);
+                        kr[s][l] = w;
+                        *(uint4*)(kt + 1024 * l + 16 * lane) = w;
+                    }
+                }
+            } else if (col == r) {
 #pragma unroll
                 for (int l = 0; l < T::LOADS; ++l) {
                     const int e0 = (64 * l + 16 * grp) / T::W;   // first element of the chunk
-                    uint4 w;
-                    if constexpr (KV == DT_BF16) w = ld16(knew + 2 * e0);
-                    else w = encode16<KV>(knew + (int64_t)src_w * e0, a.new_dtype,
-                                          __fdiv_rn(1.0f, ksc));
+                    const uint4 w = encode16<KV>(knew + (int64_t)src_w * e0, a.new_dtype,
+                                                 __fdiv_rn(1.0f, ksc));
                     kr[s][l] = w;
                     *(uint4*)(kt + r * T::ROWB + 64 * l + 16 * grp) = w;
                 }
@@ -568,12 +598,23 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
                 *(bf16x8*)(stage + lds_off<HD>(vrow[l], vcb[l] + 1)) = v1;
             }
         }
+        if constexpr (KST) {
+            // K tile into LDS: row r's 16-B chunk c at chunk c ^ kswz(r), so
+            // that both this write (a 16-lane group covers one 256-B row, or
+            // two 128-B rows) and the operand read below (16 lanes: 16 rows,
+            // one chunk each) are free of bank conflicts
+#pragma unroll
+            for (int l = 0; l < T::LOADS; ++l)
+                *(uint4*)(kstage + vrow[l] * T::ROWB +
+                          16 * ((lane % T::CPRB) ^ kswz<HD>(vrow[l]))) = kr[s][l];
+        }
         // scores S^T = K . Q^T
         f32x4 st = {0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < T::NCH; ++c) {
             bf16x8 kop;
-            if constexpr (KV == DT_BF16) kop = kv_operand_from_bytes<KV>(kr[s][c], 0);
+            if constexpr (KST)
+                kop = *(const bf16x8*)(kstage + col * T::ROWB + 16 * ((4 * c + grp) ^ kswz<HD>(col)));
             else kop = kv_operand_from_bytes<KV>(kr[s][c / 2], c % 2);
             st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[c], st, 0, 0, 0);
             if (QT == DT_F32) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
@@ -614,19 +655,36 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
         }
         l_run += psum;
 
+        // P split into bf16 hi + lo (the weights keep ~16 bits). Lane (h, G)
+        // holds tokens 4 G .. 4 G + 3 of head h as H_G (hi) and L_G (lo);
+        // the packed B operand needs, per lane row G, k = 8 G .. 8 G + 7 =
+        // [H0 H1], [H2 H3], [L0 L1], [L2 L3]: a permlane32 swap of (H, L)
+        // then a permlane16 swap regroups them.
         uint32_t hi16[4], lo16[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) split_bf16(pe[e] * vsc, hi16[e], lo16[e]);
-        const s16x4 phi = {(short)hi16[0], (short)hi16[1], (short)hi16[2], (short)hi16[3]};
-        const s16x4 plo = {(short)lo16[0], (short)lo16[1], (short)lo16[2], (short)lo16[3]};
+        uint32_t H[2] = {hi16[0] | (hi16[1] << 16), hi16[2] | (hi16[3] << 16)};
+        uint32_t L[2] = {lo16[0] | (lo16[1] << 16), lo16[2] | (lo16[3] << 16)};
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto x = __builtin_amdgcn_permlane32_swap(H[w], L[w], false, false);
+            const auto y = __builtin_amdgcn_permlane16_swap(x[0], x[1], false, false);
+            H[w] = y[0];
+            L[w] = y[1];
+        }
+        const u32x4 pb4 = {H[0], H[1], L[0], L[1]};
+        const bf16x8 pop = __builtin_bit_cast(bf16x8, pb4);
 
-        // O^T += V^T . P^T
+        // O^T += [V^T | V^T] . [P_hi ; P_lo]
 #pragma unroll
         for (int t = 0; t < T::NT; ++t) {
-            const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(stage + trd[t]));
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo, acc[t], 0, 0, 0);
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(stage + trd0[t]));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(stage + trd1[t]));
+            const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pop,
+                                                              acc[t], 0, 0, 0);
         }
         if (seg_last || i == cnt - 1) flush(seg, piece_whole && seg_last);
     };
