@@ -66,6 +66,9 @@ def parse_args(argv=None):
     ap.add_argument("--two-calls", dest="fused", action="store_false", default=True,
                     help="pda_kv_append + pda_paged_decode_attn per step instead of one fused "
                          "pda_decode_step launch (the default; identical results)")
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="single attention calls timed after a 1 GiB cache-evicting write "
+                         "(median / p10 / p90 reported; 0 skips)")
     ap.add_argument("--graph", dest="graph", action="store_true", default=False,
                     help="replay the step from a captured HIP graph (eager launches by "
                          "default: on this stack a replay adds ~6 us per step)")
@@ -341,6 +344,23 @@ def main(argv=None) -> int:
     att_ms = timed_calls(attend, K)
     app_ms = timed_calls(append, K)
 
+    def cold_calls(fn, iters):
+        """One call per iteration, each after a 1 GiB scratch write that evicts
+        the L2s and the 256 MB Infinity Cache; HIP events around the call."""
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for a, b in ev:
+            scratch.fill_(1.0)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        del scratch
+        return [a.elapsed_time(b) for a, b in ev]
+
+    cold_ms = [] if args.cold_iters <= 0 else cold_calls(attend, args.cold_iters)
+
     sb = acc.step_bytes(inp.ctx, n_q=w.n_q, n_kv=w.n_kv, d_h=w.d_h, block_size=w.block_size,
                         kv_dtype=w.kv_dtype, q_dtype=w.q_dtype,
                         new_dtype=synth.BF16 if w.kv_dtype != synth.F32 else synth.F32,
@@ -405,10 +425,18 @@ def main(argv=None) -> int:
                         "append_avg": round(_pct(app_ms, 50) * 1e3, 2),
                         "attention_avg": round(att_avg * 1e3, 2),
                         "attention_avg_min": round(min(att_ms) * 1e3, 2),
-                        "attention_avg_max": round(max(att_ms) * 1e3, 2)},
+                        "attention_avg_max": round(max(att_ms) * 1e3, 2),
+                        **({} if not cold_ms else {
+                            "attention_cold_median": round(_pct(cold_ms, 50) * 1e3, 2),
+                            "attention_cold_p10": round(_pct(cold_ms, 10) * 1e3, 2),
+                            "attention_cold_p90": round(_pct(cold_ms, 90) * 1e3, 2)})},
+        "cold_GBps_median": (None if not cold_ms else
+                             round(sb.attention / (_pct(cold_ms, 50) * 1e-3) / 1e9, 1)),
         "timing": ("fused decode step; " if args.fused else "") +
                   ("graph replay of the step" if graph is not None else "eager launches") +
-                  "; per-call averages from back-to-back calls between two HIP events",
+                  "; per-call averages from back-to-back calls between two HIP events" +
+                  (f"; cold: {len(cold_ms)} single calls, each after a 1 GiB cache-evicting "
+                   "write" if cold_ms else ""),
         "bytes_per_step": {"attention": sb.attention, "attention_unique": sb.attention_unique,
                            "step": sb.step, "kv_read": sb.kv_read},
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attn (attention + merge)",

@@ -26,17 +26,20 @@
 //
 // Per 16-token block and wave:
 //   S^T[16 tok][16 heads] = K_tile[16][d_h] . Q^T[d_h][16]  -- MFMA 16x16x32 bf16;
-//     K goes from HBM straight into the A-operand registers: lane (t, grp)
-//     loads 16 contiguous bytes of token row t, so each load instruction
-//     covers 16 rows x 64 contiguous bytes; Q sits in the B operand with the
-//     same element order (the contraction order over d_h is free).
+//     a bf16 K tile is loaded with contiguous 1 KiB-per-instruction loads and
+//     passed through an XOR-swizzled LDS tile into the A-operand layout; an
+//     8-bit tile goes from HBM straight into the A operand (lane (t, grp)
+//     holds contiguous bytes of token row t) and is converted in registers.
+//     Q sits in the B operand with the same element order (the contraction
+//     order over d_h is free).
 //   The S^T accumulator layout puts 4 tokens of one head in each lane, which
 //   is exactly the B-operand layout of the value product, so the
 //   probabilities never move between lanes.
-//   O^T[d_h][16 heads] += V^T[d_h][16 tok] . P^T[16 tok][16]  -- MFMA 16x16x16
-//     bf16; V is staged through LDS (XOR-swizzled rows, conflict-free) and
-//     read back transposed with ds_read_b64_tr_b16. P is split into bf16
-//     hi + lo parts (two MFMAs) so the weights keep ~16 bits; Q in fp32 is
+//   O^T[d_h][16 heads] += [V^T | V^T][d_h][32] . [P_hi; P_lo][32][16]  -- one
+//     MFMA 16x16x32 bf16 per 16 columns; V is staged through LDS (XOR-swizzled
+//     rows, conflict-free) and read back transposed with ds_read_b64_tr_b16.
+//     P is split into bf16 hi + lo parts so the weights keep ~16 bits; the
+//     doubled V operand folds both parts into one instruction. Q in fp32 is
 //     split the same way.
 //   8-bit caches are converted to bf16 in registers (exact), the K scale is
 //   folded into the score multiplier and the V scale into P.
