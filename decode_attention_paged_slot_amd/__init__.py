@@ -19,7 +19,7 @@ _BINDING_NAMES = (
     "kv_append", "kv_append_quant",
     "attn_desc", "attn_workspace_size", "attn_plan", "workspace_for",
     "paged_decode_attn", "paged_decode_attn_quant", "lse_merge",
-    "decode_step", "decode_step_quant",
+    "decode_step", "decode_step_quant", "paged_decode_attn_prefix", "decode_step_prefix",
 )
 
 __all__ = list(_BINDING_NAMES)

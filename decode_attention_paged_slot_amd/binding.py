@@ -61,7 +61,8 @@ class AttnDesc(ctypes.Structure):
                 ("out_dtype", ctypes.c_int32), ("max_context", ctypes.c_int32),
                 ("num_partitions", ctypes.c_int32), ("total_context", ctypes.c_int64),
                 ("reuse_prefix_blocks", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("sink_tokens", ctypes.c_int32), ("new_dtype", ctypes.c_int32)]
+                ("sink_tokens", ctypes.c_int32), ("new_dtype", ctypes.c_int32),
+                ("prefix_blocks", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -91,6 +92,12 @@ _SIGS = {
                                ctypes.POINTER(AttnDesc), _vp, _sz, _vp]),
     "pda_decode_step_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                      _vp, ctypes.POINTER(AttnDesc), _vp, _sz, _vp]),
+    "pda_paged_decode_attn_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            ctypes.c_float, _vp, ctypes.POINTER(AttnDesc), _vp,
+                                            _sz, _vp]),
+    "pda_decode_step_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_float, _vp, ctypes.POINTER(AttnDesc), _vp, _sz,
+                                      _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -170,7 +177,8 @@ def kv_append_quant(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_sca
 def attn_desc(q, k_cache, block_table, *, max_context: int, out_dtype: int = F32,
               kv_dtype: Optional[int] = None, num_partitions: int = 0,
               total_context: int = 0, reuse_prefix_blocks: int = 0, window: int = 0,
-              sink_tokens: int = 0, new_dtype: Optional[int] = None) -> AttnDesc:
+              sink_tokens: int = 0, new_dtype: Optional[int] = None,
+              prefix_blocks: int = 0) -> AttnDesc:
     B, n_q, d_h = q.shape
     nb, n_kv, bs, d2 = k_cache.shape
     assert d2 == d_h
@@ -178,7 +186,7 @@ def attn_desc(q, k_cache, block_table, *, max_context: int, out_dtype: int = F32
     return AttnDesc(B, n_q, n_kv, d_h, bs, int(block_table.shape[1]), nb, kvd, dtype_code(q),
                     out_dtype, int(max_context), int(num_partitions), int(total_context),
                     int(reuse_prefix_blocks), int(window), int(sink_tokens),
-                    kvd if new_dtype is None else int(new_dtype))
+                    kvd if new_dtype is None else int(new_dtype), int(prefix_blocks))
 
 
 def attn_workspace_size(desc: AttnDesc) -> int:
@@ -274,6 +282,38 @@ def decode_step_quant(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block
                                       _ptr(block_table), _ptr(context_lens), float(scale),
                                       _ptr(out), ctypes.byref(desc), _ptr(workspace), ws_bytes,
                                       _stream(stream)), "pda_decode_step_quant")
+
+
+def paged_decode_attn_prefix(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                             prefix_table, prefix_lens, scale: float, out, *, desc: AttnDesc,
+                             workspace=None, stream=None) -> None:
+    """pda_paged_decode_attn_prefix: attention with a shared prefix read once.
+    prefix_table [desc.prefix_blocks] int32, prefix_lens [B] int32; k_scale /
+    v_scale [NB, n_kv] f32 for 8-bit caches, None for bf16."""
+    if workspace is None:
+        workspace = workspace_for(desc, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pda_paged_decode_attn_prefix(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                             _ptr(context_lens), _ptr(prefix_table),
+                                             _ptr(prefix_lens), float(scale), _ptr(out),
+                                             ctypes.byref(desc), _ptr(workspace), ws_bytes,
+                                             _stream(stream)), "pda_paged_decode_attn_prefix")
+
+
+def decode_step_prefix(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                       context_lens, prefix_table, prefix_lens, scale: float, out, *,
+                       desc: AttnDesc, workspace=None, stream=None) -> None:
+    """pda_decode_step_prefix: the fused decode step with a shared prefix read once."""
+    if workspace is None:
+        workspace = workspace_for(desc, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pda_decode_step_prefix(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                       _ptr(block_table), _ptr(context_lens), _ptr(prefix_table),
+                                       _ptr(prefix_lens), float(scale), _ptr(out),
+                                       ctypes.byref(desc), _ptr(workspace), ws_bytes,
+                                       _stream(stream)), "pda_decode_step_prefix")
 
 
 def lse_merge(part_o, part_ml, out, *, stream=None) -> None:

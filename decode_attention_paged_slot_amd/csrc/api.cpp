@@ -80,6 +80,8 @@ Plan make_partition_plan(const pda_attn_desc& d) {
     return p;
 }
 
+Plan make_stream_plan_split(const pda_attn_desc& d, int64_t S, int64_t t_est);
+
 // Stream plan (16-bit and 8-bit caches). Measured on MI355X: the step runs
 // at its best when every compute unit holds the same amount of work, and one
 // workgroup of four streaming waves per compute unit already saturates HBM
@@ -95,7 +97,28 @@ Plan make_stream_plan(const pda_attn_desc& d) {
     const int64_t t_est = (int64_t)d.n_kv *
         (d.total_context > 0 ? ceil_div(d.total_context, d.block_size) + d.B : d.B * nblk_max);
     Plan p{1, (int32_t)std::max<int64_t>(nblk_max, 1), (int32_t)S, 0, 1};
+    if (d.prefix_blocks > 0) {
+        // with a shared prefix every row's suffix goes through the merge, so
+        // the split bookkeeping is always on; "unsplit" is one range per segment
+        Plan q = p;
+        if (d.num_partitions != 1) q = make_stream_plan_split(d, S, t_est);
+        if (!q.split) {
+            q.nw = (int32_t)std::min<int64_t>(std::max<int64_t>(S, 1), kMaxStreamWaves);
+            q.split = 1;
+            q.P = q.nw;
+            q.bpp = (int32_t)std::max<int64_t>(1, (t_est + q.nw - 1) / q.nw);
+        }
+        return q;
+    }
     if (d.num_partitions == 1) return p;
+    return make_stream_plan_split(d, S, t_est);
+}
+
+// The split part of the stream plan (see make_stream_plan).
+Plan make_stream_plan_split(const pda_attn_desc& d, int64_t S, int64_t t_est) {
+    const int64_t nblk_max = std::min<int64_t>(
+        ceil_div(std::max<int64_t>(d.max_context, 1), d.block_size), d.max_blocks_per_seq);
+    Plan p{1, (int32_t)std::max<int64_t>(nblk_max, 1), (int32_t)S, 0, 1};
     int64_t nw;
     if (d.num_partitions > 1) {
         nw = d.num_partitions;
@@ -122,7 +145,7 @@ Plan make_plan(const pda_attn_desc& d) {
 }
 
 WsLayout ws_layout(const pda_attn_desc& d, const Plan& p) {
-    WsLayout w{0, 0, 0, 0};
+    WsLayout w{0, 0, 0, 0, 0, 0};
     if (p.stream) {
         if (!p.split) return w;
         const size_t S = (size_t)d.B * d.n_kv;
@@ -132,6 +155,13 @@ WsLayout ws_layout(const pda_attn_desc& d, const Plan& p) {
         w.part_ml_off = align256(slots * g * d.d_h * sizeof(float));
         w.seg_info_off = w.part_ml_off + align256(slots * g * 2 * sizeof(float));
         w.bytes = w.seg_info_off + align256(S * 2 * sizeof(int32_t));
+        if (d.prefix_blocks > 0) {
+            const size_t chunks = (size_t)ceil_div(d.prefix_blocks, kPrefixChunk);
+            const size_t rows = (size_t)d.B * d.n_q;
+            w.pre_o_off = w.bytes;
+            w.pre_ml_off = w.pre_o_off + align256(chunks * rows * d.d_h * sizeof(float));
+            w.bytes = w.pre_ml_off + align256(chunks * rows * 2 * sizeof(float));
+        }
         return w;
     }
     if (p.P <= 1) return w;
@@ -148,7 +178,10 @@ using namespace pda;
 
 namespace {
 
-int32_t check_attn_desc(const pda_attn_desc* d, bool quant) {
+// Which call a descriptor is checked for.
+enum CallKind { kPlain, kQuant, kPrefix, kQuery };
+
+int32_t check_attn_desc(const pda_attn_desc* d, CallKind kind) {
     if (!d) {
         set_error("attention descriptor is NULL");
         return PDA_EINVAL;
@@ -177,10 +210,32 @@ int32_t check_attn_desc(const pda_attn_desc* d, bool quant) {
                   d->max_blocks_per_seq, d->num_blocks, d->max_context);
         return PDA_EINVAL;
     }
-    const bool kv_ok = quant ? (d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8)
-                             : (d->kv_dtype == PDA_F32 || d->kv_dtype == PDA_BF16);
+    const bool eight = d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8;
+    const bool wide = d->kv_dtype == PDA_F32 || d->kv_dtype == PDA_BF16;
+    const bool kv_ok = kind == kQuant    ? eight
+                       : kind == kPlain  ? wide
+                       : kind == kPrefix ? (eight || d->kv_dtype == PDA_BF16)
+                                         : (eight || wide);
     if (!kv_ok) {
         set_error("kv_dtype %d not valid for this call", d->kv_dtype);
+        return PDA_EINVAL;
+    }
+    if (d->prefix_blocks < 0 || d->prefix_blocks > d->max_blocks_per_seq ||
+        d->prefix_blocks > kMaxPrefixBlocks) {
+        set_error("prefix_blocks=%d outside [0, min(max_blocks_per_seq, %d)]", d->prefix_blocks,
+                  kMaxPrefixBlocks);
+        return PDA_EINVAL;
+    }
+    if (kind == kPrefix && d->prefix_blocks == 0) {
+        set_error("shared-prefix call with prefix_blocks == 0");
+        return PDA_EINVAL;
+    }
+    if ((kind == kPlain || kind == kQuant) && d->prefix_blocks != 0) {
+        set_error("prefix_blocks=%d is for the *_prefix calls only", d->prefix_blocks);
+        return PDA_EINVAL;
+    }
+    if (d->prefix_blocks > 0 && (d->window != 0 || d->kv_dtype == PDA_F32)) {
+        set_error("a shared prefix needs window == 0 and a BF16 / FP8_E4M3 / INT8 cache");
         return PDA_EINVAL;
     }
     if ((d->q_dtype != PDA_F32 && d->q_dtype != PDA_BF16) ||
@@ -235,10 +290,12 @@ int32_t debug_check(const pda_attn_desc* d, const int32_t* block_table,
 int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
                  const float* v_scale, const int32_t* block_table, const int32_t* context_lens,
                  float scale, void* out, const pda_attn_desc* d, void* workspace,
-                 size_t ws_bytes, void* stream, bool quant, const void* k_new = nullptr,
-                 const void* v_new = nullptr, bool fused = false) {
-    int32_t rc = check_attn_desc(d, quant);
+                 size_t ws_bytes, void* stream, CallKind kind, const void* k_new = nullptr,
+                 const void* v_new = nullptr, bool fused = false,
+                 const int32_t* prefix_table = nullptr, const int32_t* prefix_lens = nullptr) {
+    int32_t rc = check_attn_desc(d, kind);
     if (rc != PDA_OK) return rc;
+    const bool quant = d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8;
     if (fused) {
         const bool ok = quant ? (d->new_dtype == PDA_F32 || d->new_dtype == PDA_BF16)
                               : d->new_dtype == d->kv_dtype;
@@ -253,7 +310,8 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
         return PDA_EINVAL;
     }
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
-        (quant && (!k_scale || !v_scale))) {
+        (quant && (!k_scale || !v_scale)) ||
+        (kind == kPrefix && (!prefix_table || !prefix_lens))) {
         set_error("NULL device pointer");
         return PDA_EINVAL;
     }
@@ -309,7 +367,25 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     a.k_new = fused ? k_new : nullptr;
     a.v_new = fused ? v_new : nullptr;
     a.new_dtype = d->new_dtype;
+    const bool prefix = kind == kPrefix;
+    // Split units charged per (sequence, KV head) segment for its fixed costs
+    // (a query load, a partial write, a fused append). Measured on MI355X:
+    // with a shared prefix many rows keep only a block or two of their own,
+    // and a wave crossing dozens of such segments set the kernel's time until
+    // each segment start was charged as 4 blocks; with whole rows the
+    // segments are long and equal block counts per wave are best.
+    a.seg_cost = std::max(env_int("PDA_SEGMENT_COST", prefix ? 4 : 0), 0);
+    a.prefix_table = prefix ? prefix_table : nullptr;
+    a.prefix_lens = prefix ? prefix_lens : nullptr;
+    a.prefix_blocks = prefix ? d->prefix_blocks : 0;
+    a.pre_o = prefix ? (float*)((char*)workspace + ws.pre_o_off) : nullptr;
+    a.pre_ml = prefix ? (float*)((char*)workspace + ws.pre_ml_off) : nullptr;
     hipError_t e;
+    if (prefix) {
+        // the shared blocks first: they are never the block a fused step writes
+        e = launch_attn_prefix(a, s);
+        if (e != hipSuccess) return hip_fail("prefix attention launch", e);
+    }
     if (plan.stream) {
         e = launch_attn_mfma(a, s);
         if (e != hipSuccess) return hip_fail("attention launch", e);
@@ -410,8 +486,7 @@ int32_t pda_attn_workspace_size(const pda_attn_desc* d, size_t* bytes) {
         set_error("bytes is NULL");
         return PDA_EINVAL;
     }
-    const bool quant = d && (d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8);
-    int32_t rc = check_attn_desc(d, quant);
+    int32_t rc = check_attn_desc(d, kQuery);
     if (rc != PDA_OK) return rc;
     *bytes = ws_layout(*d, make_plan(*d)).bytes;
     return PDA_OK;
@@ -423,8 +498,7 @@ int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
         set_error("NULL output pointer");
         return PDA_EINVAL;
     }
-    const bool quant = d && (d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8);
-    int32_t rc = check_attn_desc(d, quant);
+    int32_t rc = check_attn_desc(d, kQuery);
     if (rc != PDA_OK) return rc;
     const Plan p = make_plan(*d);
     *num_partitions = p.P;
@@ -437,7 +511,7 @@ int32_t pda_paged_decode_attn(const void* q, const void* k_cache, const void* v_
                               void* out, const pda_attn_desc* d, void* workspace,
                               size_t ws_bytes, void* stream) {
     return run_attn(q, k_cache, v_cache, nullptr, nullptr, block_table, context_lens, scale, out,
-                    d, workspace, ws_bytes, stream, false);
+                    d, workspace, ws_bytes, stream, kPlain);
 }
 
 int32_t pda_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
@@ -446,7 +520,7 @@ int32_t pda_paged_decode_attn_quant(const void* q, const void* k_cache, const vo
                                     float scale, void* out, const pda_attn_desc* d,
                                     void* workspace, size_t ws_bytes, void* stream) {
     return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
-                    d, workspace, ws_bytes, stream, true);
+                    d, workspace, ws_bytes, stream, kQuant);
 }
 
 int32_t pda_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -454,7 +528,7 @@ int32_t pda_decode_step(const void* q, const void* k_new, const void* v_new, voi
                         float scale, void* out, const pda_attn_desc* d, void* workspace,
                         size_t ws_bytes, void* stream) {
     return run_attn(q, k_cache, v_cache, nullptr, nullptr, block_table, context_lens, scale, out,
-                    d, workspace, ws_bytes, stream, false, k_new, v_new, true);
+                    d, workspace, ws_bytes, stream, kPlain, k_new, v_new, true);
 }
 
 int32_t pda_decode_step_quant(const void* q, const void* k_new, const void* v_new,
@@ -464,7 +538,30 @@ int32_t pda_decode_step_quant(const void* q, const void* k_new, const void* v_ne
                               const pda_attn_desc* d, void* workspace, size_t ws_bytes,
                               void* stream) {
     return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
-                    d, workspace, ws_bytes, stream, true, k_new, v_new, true);
+                    d, workspace, ws_bytes, stream, kQuant, k_new, v_new, true);
+}
+
+int32_t pda_paged_decode_attn_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     const int32_t* prefix_table, const int32_t* prefix_lens,
+                                     float scale, void* out, const pda_attn_desc* d,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+    return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
+                    d, workspace, ws_bytes, stream, kPrefix, nullptr, nullptr, false,
+                    prefix_table, prefix_lens);
+}
+
+int32_t pda_decode_step_prefix(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, const float* k_scale,
+                               const float* v_scale, const int32_t* block_table,
+                               const int32_t* context_lens, const int32_t* prefix_table,
+                               const int32_t* prefix_lens, float scale, void* out,
+                               const pda_attn_desc* d, void* workspace, size_t ws_bytes,
+                               void* stream) {
+    return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
+                    d, workspace, ws_bytes, stream, kPrefix, k_new, v_new, true, prefix_table,
+                    prefix_lens);
 }
 
 int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,

@@ -73,25 +73,10 @@ struct Tr {
     static constexpr int CPRB = ROWB / 16;              // 16-B chunks per cache row
 };
 
-// XOR swizzle of the bf16 K staging tile (16 rows of 2 * HD bytes).
-template <int HD>
-__device__ __forceinline__ constexpr int kswz(int r) {
-    return HD == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-
 // First element of QK chunk c held by lane group grp (8 consecutive elements).
 template <int HD, int KV>
 __device__ __forceinline__ constexpr int dmap(int c, int grp) {
     return KV == DT_BF16 ? 32 * c + 8 * grp : 64 * (c / 2) + 16 * grp + 8 * (c % 2);
-}
-
-// Byte offset of (row t, 16-B chunk cb) in a bf16 LDS tile; the XOR keeps the
-// 16 rows of a transposed read on distinct banks.
-template <int HD>
-__device__ __forceinline__ int lds_off(int t, int cb) {
-    constexpr int CPR = HD / 8, RPS = 256 / (HD * 2);
-    const int f = 2 * ((t / RPS) % (CPR / 2));
-    return t * (HD * 2) + 16 * (cb ^ f);
 }
 
 __device__ __forceinline__ uint4 ld16(const char* p) { return *(const uint4*)p; }
@@ -107,86 +92,41 @@ __device__ __forceinline__ uint4 ld16_stream(const char* p) {
 }
 
 
-// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane
-// rows of a wave) with the gfx950 row swaps: permlane16_swap exchanges rows
-// 1 <-> 0 and 3 <-> 2 between its two operands, permlane32_swap the two
-// halves; with both operands equal, each result pair holds a lane's value
-// and its partner's.
-__device__ __forceinline__ float max_rows4(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float sum_rows4(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
+// The new row's elements this lane holds (8 bytes of the source row: 4 bf16
+// or 2 fp32 values) -> their cache codes, encoded with the destination
+// block's reciprocal scale exactly as the quantized append encodes them:
+// y = x * fp32(1 / scale), round to nearest even, saturate. Returns the codes
+// packed low byte first (4 or 2 of them).
 template <int KV>
-__device__ __forceinline__ bf16x8 kv_operand_from_bytes(uint4 w, int half) {
-    if (KV == DT_BF16) {
-        return __builtin_bit_cast(bf16x8, w);
-    } else {
-        const uint32_t a = half ? w.z : w.x;
-        const uint32_t b = half ? w.w : w.y;
-        u32x2 lo, hi;
-        if (KV == DT_FP8) { lo = fp8x4_to_bf16x4(a); hi = fp8x4_to_bf16x4(b); }
-        else { lo = int8x4_to_bf16x4(a); hi = int8x4_to_bf16x4(b); }
-        u32x4 r = {lo.x, lo.y, hi.x, hi.y};
-        return __builtin_bit_cast(bf16x8, r);
-    }
-}
-
-
-// 16 new-row elements (fp32 or bf16 at `src`) -> 16 cache codes, encoded with
-// the destination block's reciprocal scale exactly as the quantized append
-// encodes them: y = x * fp32(1 / scale), round to nearest even, saturate.
-template <int KV>
-__device__ __forceinline__ uint4 encode16(const char* src, int src_dtype, float inv) {
-    float x[16];
+__device__ __forceinline__ uint32_t encode_lane(uint2 w, int src_dtype, float inv) {
+    float x[4];
+    int n;
     if (src_dtype == DT_F32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 f = *(const float4*)(src + 16 * i);
-            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
-        }
+        x[0] = __uint_as_float(w.x);
+        x[1] = __uint_as_float(w.y);
+        n = 2;
     } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint4 w = *(const uint4*)(src + 16 * i);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                x[8 * i + 2 * k] = bf16_lo_to_f32(ws[k]);
-                x[8 * i + 2 * k + 1] = bf16_hi_to_f32(ws[k]);
-            }
-        }
+        x[0] = bf16_lo_to_f32(w.x);
+        x[1] = bf16_hi_to_f32(w.x);
+        x[2] = bf16_lo_to_f32(w.y);
+        x[3] = bf16_hi_to_f32(w.y);
+        n = 4;
     }
-    uint32_t packed[4];
+    uint32_t packed = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float y = __fmul_rn(x[4 * k + e], inv);
+    for (int e = 0; e < 4; ++e) {
+        if (e < n) {
+            const float y = __fmul_rn(x[e], inv);
             const uint32_t code = KV == DT_FP8 ? quant_fp8_e4m3(y) : ((uint32_t)quant_int8(y) & 0xFFu);
-            w |= code << (8 * e);
+            packed |= code << (8 * e);
         }
-        packed[k] = w;
     }
-    return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    return packed;
 }
 
 // Per-block metadata, lane i of a 64-block batch describing block i.
-//   info bit 5 first block of its segment, bit 6 last block of its
+//   info bit 4 the row has a shared prefix (its pieces always go through
+//   the merge), bit 5 first block of its segment, bit 6 last block of its
 //   segment, bit 7 shared (cache-retaining loads), bits 8.. segment index.
 // A segment lists only the blocks holding attended positions (all blocks of
 // the row, or its sink and window blocks with a sliding window).
@@ -198,16 +138,19 @@ struct Meta {
 };
 
 template <int HD, int KV, int QT>
-__global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mfma(AttnArgs a) {
     using T = Tr<HD, KV>;
     constexpr bool QUANT = KV != DT_BF16;
     // per wave: the V tile (bf16) and, for bf16 caches, the K tile
     constexpr bool KST = KV == DT_BF16;
     __shared__ __attribute__((aligned(16))) char stage_all[4 * T::LTILE * (KST ? 2 : 1)];
-    __shared__ int wsum[4];
+    // fused decode step: per wave, the new K and V rows (up to 512 B each)
+    __shared__ __attribute__((aligned(16))) char newrow_all[4 * 2 * 512];
+    __shared__ int wsum[4], wsumu[4];
     extern __shared__ int dyn_lds[];
     int* pre = dyn_lds;             // [B + 1] exclusive prefix of blocks per sequence
     int* nn = dyn_lds + a.B + 1;    // [B] context length, -1 for an invalid one
+    int* preu = dyn_lds + 2 * a.B + 1;   // [B + 1] exclusive prefix of split units per sequence
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -217,52 +160,102 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     const int B = a.B;
     const int n_kv = a.n_kv;
 
-    // ---- per-sequence block counts and their exclusive prefix (LDS)
+    // ---- per-sequence block counts and their exclusive prefixes (LDS): in
+    // blocks, and in split units, where every non-empty segment also counts
+    // seg_cost units for its fixed costs (query load, partial write), so that
+    // waves crossing many short segments get fewer blocks
+    const int C = a.seg_cost;
     {
         const int R = (B + kAttnThreads - 1) / kAttnThreads;
         const int r0 = threadIdx.x * R;
-        int local = 0;
+        auto seg_blocks = [&](int b, int n) {
+            // with a shared prefix, only the row's blocks after it are streamed here
+            const int pl = a.prefix_lens == nullptr
+                               ? (n < 0 || n > a.max_blocks * 16 ? -1 : 0)
+                               : row_prefix_len(n, a.prefix_lens[b], a.max_blocks,
+                                                a.prefix_blocks);
+            return pl < 0 ? -1 : row_blocks(n, a.window, a.sinks).count - pl;
+        };
+        int local = 0, localu = 0;
         for (int r = 0; r < R; ++r) {
             const int b = r0 + r;
             if (b < B) {
                 const int n = a.context_lens[b];
-                const bool bad = n < 0 || n > a.max_blocks * 16;
-                nn[b] = bad ? -1 : n;
-                local += bad ? 0 : row_blocks(n, a.window, a.sinks).count;
+                const int c = seg_blocks(b, n);
+                nn[b] = c < 0 ? -1 : n;
+                const int cb = max(c, 0);
+                local += cb;
+                localu += cb + (cb > 0 ? C : 0);
             }
         }
-        int incl = local;
+        int incl = local, inclu = localu;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
+            const int yu = __shfl_up(inclu, o, 64);
+            if (lane >= o) {
+                incl += y;
+                inclu += yu;
+            }
         }
-        if (lane == 63) wsum[wave] = incl;
+        if (lane == 63) {
+            wsum[wave] = incl;
+            wsumu[wave] = inclu;
+        }
         __syncthreads();
-        int run = incl - local;
-        for (int w = 0; w < wave; ++w) run += wsum[w];
+        int run = incl - local, runu = inclu - localu;
+        for (int w = 0; w < wave; ++w) {
+            run += wsum[w];
+            runu += wsumu[w];
+        }
         for (int r = 0; r < R; ++r) {
             const int b = r0 + r;
             if (b < B) {
                 pre[b] = run;
-                run += nn[b] < 0 ? 0 : row_blocks(nn[b], a.window, a.sinks).count;
+                preu[b] = runu;
+                const int cb = nn[b] < 0 ? 0 : max(seg_blocks(b, nn[b]), 0);
+                run += cb;
+                runu += cb + (cb > 0 ? C : 0);
             }
         }
-        if (threadIdx.x == kAttnThreads - 1) pre[B] = run;
+        if (threadIdx.x == kAttnThreads - 1) {
+            pre[B] = run;
+            preu[B] = runu;
+        }
         __syncthreads();
     }
     const int64_t T_all = (int64_t)n_kv * pre[B];
-    // never more ranges than blocks: every range in use is non-empty, so the
+    const int64_t T_u = (int64_t)n_kv * preu[B];
+    // never more ranges than units: every range in use is non-empty, so the
     // pieces of a segment come from consecutive waves without gaps
-    const int NW = (int)max((int64_t)1, min((int64_t)a.nw, T_all));
+    const int NW = (int)max((int64_t)1, min((int64_t)a.nw, T_u));
     const int wg = blockIdx.x * 4 + wave;   // global wave index
 
-    // ---- this wave's range [lo, hi) of the flattened axis
-    int64_t lo = 0, hi = 0;
+    // first block position at or after unit u: segment s of row b spans units
+    // [U, U + C + nb), its fixed-cost units first, then one unit per block
+    auto unit_to_block = [&](int64_t u) -> int64_t {
+        if (u >= T_u) return T_all;
+        int l = 0, r = B - 1;   // last sequence whose first unit is <= u (non-empty)
+        while (l < r) {
+            const int mid = (l + r + 1) >> 1;
+            if ((int64_t)n_kv * preu[mid] <= u) l = mid;
+            else r = mid - 1;
+        }
+        const int nb = pre[l + 1] - pre[l];
+        const int64_t r0 = u - (int64_t)n_kv * preu[l];
+        const int j = (int)(r0 / (nb + C));
+        const int off = (int)(r0 - (int64_t)j * (nb + C));
+        return (int64_t)n_kv * pre[l] + (int64_t)j * nb + max(0, off - C);
+    };
+
+    // ---- this wave's range [lo, hi) of the flattened block axis
+    int64_t lo = 0, hi = 0, lo_u = 0, hi_u = 0;
     if (a.split) {
         if (wg < NW) {
-            lo = (int64_t)wg * T_all / NW;
-            hi = (int64_t)(wg + 1) * T_all / NW;
+            lo_u = (int64_t)wg * T_u / NW;
+            hi_u = (int64_t)(wg + 1) * T_u / NW;
+            lo = C == 0 ? lo_u : unit_to_block(lo_u);   // with no segment cost, units are blocks
+            hi = C == 0 ? hi_u : unit_to_block(hi_u);
         }
     } else if (wg < B * n_kv) {
         const int b = wg / n_kv, j = wg - (wg / n_kv) * n_kv;
@@ -280,19 +273,19 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     };
 
     // ---- sequences without blocks (empty, or invalid length): zero / NaN rows.
-    // Split mode: such a sequence sits at position n_kv * pre[b]; the wave
-    // whose range holds that position owns it (the last wave also owns the
-    // position T_all). Unsplit mode: the wave of each of its segments.
+    // Split mode: such a sequence sits at unit n_kv * preu[b]; the wave whose
+    // unit range holds it owns it (the last wave also owns the unit T_u).
+    // Unsplit mode: the wave of each of its segments.
     if (a.split) {
         if (wg < NW) {
-            const int64_t hi_ext = (wg == NW - 1) ? T_all + 1 : hi;
+            const int64_t hi_ext = (wg == NW - 1) ? T_u + 1 : hi_u;
             int l = 0, r = B;
             while (l < r) {
                 const int mid = (l + r) >> 1;
-                if ((int64_t)n_kv * pre[mid] >= lo) r = mid;
+                if ((int64_t)n_kv * preu[mid] >= lo_u) r = mid;
                 else l = mid + 1;
             }
-            for (int b = l; b < B && (int64_t)n_kv * pre[b] < hi_ext; ++b) {
+            for (int b = l; b < B && (int64_t)n_kv * preu[b] < hi_ext; ++b) {
                 if (pre[b + 1] != pre[b]) continue;
                 write_rows((int64_t)b * a.n_q, a.n_q, nn[b] < 0 ? __builtin_nanf("") : 0.0f);
                 for (int jj = lane; jj < n_kv; jj += 64)
@@ -323,13 +316,16 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             const int r0 = x - n_kv * pre[b];
             const int j = r0 / nb;
             const int bl = r0 - j * nb;   // attended-block index within the row
-            const int blk = row_block_logical(row_blocks(nn[b], a.window, a.sinks), bl);
+            // rows with a shared prefix: their first pl blocks belong to the
+            // prefix pass, this pass starts after them (no window there)
+            const int pl = a.prefix_lens == nullptr ? 0 : a.prefix_lens[b];
+            const int blk = row_block_logical(row_blocks(nn[b], a.window, a.sinks), bl) + pl;
             int id = a.block_table[(int64_t)b * a.max_blocks + blk];
             if (id < 0 || id >= a.num_blocks) id = -1;
             const int seg = b * n_kv + j;
             m.id = id;
-            m.info = ((bl == 0) << 5) | ((bl == nb - 1) << 6) | ((blk < a.reuse_blocks) << 7) |
-                     (seg << 8);
+            m.info = ((pl > 0) << 4) | ((bl == 0) << 5) | ((bl == nb - 1) << 6) |
+                     ((blk < a.reuse_blocks) << 7) | (seg << 8);
             m.mask = (int)block_token_mask(blk, nn[b], a.window, a.sinks);
             if (QUANT && id >= 0) {
                 m.ksc = a.k_scale[(int64_t)id * n_kv + j];
@@ -440,6 +436,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
     auto vsc_of = [&](int i) { return QUANT ? meta_f(A.vsc, Bm.vsc, i) : 1.0f; };
 
     uint4 kr[kDepth][T::LOADS], vr[kDepth][T::LOADS];
+    uint2 nkr[kDepth], nvr[kDepth];   // fused step: 8 B of the new K / V row per lane
+    char* newk = newrow_all + wave * 1024;
+    char* newv = newk + 512;
+    const int new_rowb = HD * (a.new_dtype == DT_F32 ? 4 : 2);   // bytes per new row
 
     // Loads are never predicated (a partially filled final block is still a
     // whole allocated tile; its tail rows are masked after loading; an
@@ -458,6 +458,17 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
         // registers, lane (t, grp) taking 16 B of token row t
         const int koff = KST ? 16 * lane : col * T::ROWB + 16 * grp;
         const int kstep = KST ? 1024 : 64;
+        if (a.k_new != nullptr && ((info >> 6) & 1)) {
+            // the row's newest block (fused step): its new K / V rows are
+            // fetched with the tile, one coalesced 8-B piece per lane, so the
+            // patch does not wait on memory (a wave may patch many rows in a
+            // row when segments are a single block)
+            const int64_t nrow = (int64_t)((unsigned)info >> 8) * new_rowb;
+            if (8 * lane < new_rowb) {
+                nkr[s] = *(const uint2*)((const char*)a.k_new + nrow + 8 * lane);
+                nvr[s] = *(const uint2*)((const char*)a.v_new + nrow + 8 * lane);
+            }
+        }
         if ((info >> 7) & 1) {
 #pragma unroll
             for (int l = 0; l < T::LOADS; ++l) kr[s][l] = ld16(kt + koff + kstep * l);
@@ -477,10 +488,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
         if (col < g) {
             const int64_t prow = whole ? (int64_t)seg * g + col : ((int64_t)seg + wg) * g + col;
             f32x4 r[T::NT];
+            const float inv = l_tot != 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
-            for (int t = 0; t < T::NT; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[t][e] = l_tot != 0.0f ? acc[t][e] / l_tot : 0.0f;
+            for (int t = 0; t < T::NT; ++t) r[t] = acc[t] * inv;
             if (!whole) {
 #pragma unroll
                 for (int t = 0; t < T::NT; ++t)
@@ -525,10 +535,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
                 q_seg = seg;
             }
             if (a.split && seg_first && lane == 0) {
-                // record the waves covering this segment for the merge
-                const int b = seg / n_kv;
-                const int64_t end = lo + i + (pre[b + 1] - pre[b]);
-                const int last_wave = (int)((end * NW - 1) / T_all);
+                // record the waves covering this segment for the merge: the
+                // last is the wave holding the segment's last unit
+                const int b = seg / n_kv, j = seg - (seg / n_kv) * n_kv;
+                const int64_t end_u =
+                    (int64_t)n_kv * preu[b] + (int64_t)(j + 1) * (pre[b + 1] - pre[b] + C);
+                const int last_wave = (int)((end_u * NW - 1) / T_u);
                 a.seg_info[seg] = make_int2(wg, last_wave);
             }
         }
@@ -546,15 +558,35 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             const int r = (nn[b] - 1) & 15;
             char* kt = (char*)kbase + (int64_t)pb_i * block_stride + (int64_t)j * head_stride;
             char* vt = (char*)vbase + (int64_t)pb_i * block_stride + (int64_t)j * head_stride;
-            const int src_w = a.new_dtype == DT_F32 ? 4 : 2;   // bytes per new-row element
-            const char* knew = (const char*)a.k_new + (int64_t)seg * HD * src_w;
-            const char* vnew = (const char*)a.v_new + (int64_t)seg * HD * src_w;
+            // the prefetched rows into this wave's LDS buffer as cache
+            // codes (8-bit caches: each lane encodes the elements it holds),
+            // where the lanes that hold row r of the tile read their pieces
+            if (8 * lane < new_rowb) {
+                if constexpr (QUANT) {
+                    const int per = a.new_dtype == DT_F32 ? 2 : 4;   // elements per lane
+                    const uint32_t ck = encode_lane<KV>(nkr[s], a.new_dtype, __fdiv_rn(1.0f, ksc));
+                    const uint32_t cv = encode_lane<KV>(nvr[s], a.new_dtype, __fdiv_rn(1.0f, vsc));
+                    if (per == 4) {
+                        *(uint32_t*)(newk + 4 * lane) = ck;
+                        *(uint32_t*)(newv + 4 * lane) = cv;
+                    } else {
+                        *(uint16_t*)(newk + 2 * lane) = (uint16_t)ck;
+                        *(uint16_t*)(newv + 2 * lane) = (uint16_t)cv;
+                    }
+                } else {
+                    *(uint2*)(newk + 8 * lane) = nkr[s];
+                    *(uint2*)(newv + 8 * lane) = nvr[s];
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the writes have landed
+            __builtin_amdgcn_wave_barrier();
+            // newk / newv now hold row r in the cache's own bytes
             if constexpr (KST) {
 #pragma unroll
                 for (int l = 0; l < T::LOADS; ++l) {
                     if (vrow[l] == r) {   // contiguous K: same lanes as V
                         const int b0 = (1024 * l + 16 * lane) - r * T::ROWB;
-                        const uint4 w = ld16(knew + b0);
+                        const uint4 w = *(const uint4*)(newk + b0);
                         kr[s][l] = w;
                         *(uint4*)(kt + 1024 * l + 16 * lane) = w;
                     }
@@ -562,9 +594,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             } else if (col == r) {
 #pragma unroll
                 for (int l = 0; l < T::LOADS; ++l) {
-                    const int e0 = (64 * l + 16 * grp) / T::W;   // first element of the chunk
-                    const uint4 w = encode16<KV>(knew + (int64_t)src_w * e0, a.new_dtype,
-                                                 __fdiv_rn(1.0f, ksc));
+                    const uint4 w = *(const uint4*)(newk + 64 * l + 16 * grp);
                     kr[s][l] = w;
                     *(uint4*)(kt + r * T::ROWB + 64 * l + 16 * grp) = w;
                 }
@@ -572,11 +602,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
 #pragma unroll
             for (int l = 0; l < T::LOADS; ++l) {
                 if (vrow[l] == r) {
-                    const int e0 = ((1024 * l + 16 * lane) - r * T::ROWB) / T::W;
-                    uint4 w;
-                    if constexpr (KV == DT_BF16) w = ld16(vnew + 2 * e0);
-                    else w = encode16<KV>(vnew + (int64_t)src_w * e0, a.new_dtype,
-                                          __fdiv_rn(1.0f, vsc));
+                    const uint4 w = *(const uint4*)(newv + (1024 * l + 16 * lane) - r * T::ROWB);
                     vr[s][l] = w;
                     *(uint4*)(vt + 1024 * l + 16 * lane) = w;
                 }
@@ -689,9 +715,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pop,
                                                               acc[t], 0, 0, 0);
         }
-        if (seg_last || i == cnt - 1) flush(seg, piece_whole && seg_last);
+        if (seg_last || i == cnt - 1) flush(seg, piece_whole && seg_last && !((info >> 4) & 1));
     };
 
+    // the first segment's queries, in flight with the first tiles
+    q_seg = (int)((unsigned)meta_info(0) >> 8);
+    load_q(q_seg);
     int it = 0;
     if (cnt >= 2 * kDepth) {
         // prologue and steady state issue unconditionally and in slot order
@@ -720,7 +749,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) k_attn_mfma(AttnArgs a) {
 
 }  // namespace
 
-size_t attn_mfma_dyn_lds(int32_t B) { return (size_t)(2 * B + 1) * sizeof(int32_t); }
+size_t attn_mfma_dyn_lds(int32_t B) { return (size_t)(3 * B + 2) * sizeof(int32_t); }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
     const int waves = a.split ? a.nw : a.B * a.n_kv;

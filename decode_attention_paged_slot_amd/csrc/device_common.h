@@ -134,4 +134,73 @@ __device__ __forceinline__ uint32_t block_token_mask(int L, int n, int window, i
     return m;
 }
 
+
+// XOR swizzle of the bf16 K staging tile (16 rows of 2 * HD bytes).
+template <int HD>
+__device__ __forceinline__ constexpr int kswz(int r) {
+    return HD == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Byte offset of (row t, 16-B chunk cb) in a bf16 LDS tile; the XOR keeps the
+// 16 rows of a transposed read on distinct banks.
+template <int HD>
+__device__ __forceinline__ int lds_off(int t, int cb) {
+    constexpr int CPR = HD / 8, RPS = 256 / (HD * 2);
+    const int f = 2 * ((t / RPS) % (CPR / 2));
+    return t * (HD * 2) + 16 * (cb ^ f);
+}
+
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane
+// rows of a wave) with the gfx950 row swaps: permlane16_swap exchanges rows
+// 1 <-> 0 and 3 <-> 2 between its two operands, permlane32_swap the two
+// halves; with both operands equal, each result pair holds a lane's value
+// and its partner's.
+__device__ __forceinline__ float max_rows4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_rows4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int KV>
+__device__ __forceinline__ bf16x8 kv_operand_from_bytes(uint4 w, int half) {
+    if (KV == DT_BF16) {
+        return __builtin_bit_cast(bf16x8, w);
+    } else {
+        const uint32_t a = half ? w.z : w.x;
+        const uint32_t b = half ? w.w : w.y;
+        u32x2 lo, hi;
+        if (KV == DT_FP8) { lo = fp8x4_to_bf16x4(a); hi = fp8x4_to_bf16x4(b); }
+        else { lo = int8x4_to_bf16x4(a); hi = int8x4_to_bf16x4(b); }
+        u32x4 r = {lo.x, lo.y, hi.x, hi.y};
+        return __builtin_bit_cast(bf16x8, r);
+    }
+}
+
+
+// Shared-prefix length of a row as the attention kernels use it: logical
+// blocks 0 .. p - 1 of the row are the shared prefix blocks. `n` is the
+// row's context length, `pl` its requested prefix length. Returns -1 when the
+// row is invalid (n outside [0, max_blocks * 16], or a prefix that is
+// negative, longer than the prefix table, or reaching the block that holds
+// the row's newest position, which copy on write keeps private), else the
+// prefix length (0 for an empty row).
+__device__ __forceinline__ int row_prefix_len(int n, int pl, int max_blocks, int prefix_blocks) {
+    if (n < 0 || n > max_blocks * 16) return -1;
+    if (n == 0) return 0;
+    if (pl < 0 || pl > prefix_blocks || pl >= ((n + 15) >> 4)) return -1;
+    return pl;
+}
+
 }  // namespace pda

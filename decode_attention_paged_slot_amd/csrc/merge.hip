@@ -40,31 +40,48 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return v;
 }
 
-// Merge of np partials of one output row into `out_row` (HD floats or
-// bf16), columns [c0 * 4, (c0 + V) * 4) of it: partial p has statistics
-// (m, l) at ml + p * sm and output at po + p * so. Phase 1: every thread takes
-// partials p = tid, tid + 256, ... for the block-wide max M and the weights
-// w_p = l_p 2^(m_p - M), kept in LDS. Phase 2: thread (sub, c) accumulates
-// the 4-float column group c0 + c of the partials p = sub, sub + SUB, ...
-// (loads are unconditional, so they can all be in flight together; an empty
-// partial's weight is 0 and its data unused); the SUB partial sums are added
-// through LDS.
+// Merge of the partials of one output row into `out_row` (HD floats or
+// bf16), columns [c0 * 4, (c0 + V) * 4) of it. The partials come from two
+// strided runs: p < n1 has statistics (m, l) at ml1 + p * sm1 and output at
+// po1 + p * so1, p = n1 + k (k < n2) at ml2 + k * sm2 and po2 + k * so2.
+// Phase 1: every thread takes partials p = tid, tid + 256, ... for the
+// block-wide max M and the weights w_p = l_p 2^(m_p - M), kept in LDS.
+// Phase 2: thread (sub, c) accumulates the 4-float column group c0 + c of
+// the partials p = sub, sub + SUB, ... (loads are unconditional, so they can
+// all be in flight together; an empty partial's weight is 0 and its data
+// unused); the SUB partial sums are added through LDS.
+struct PieceRuns {
+    const float* po1;
+    const float* ml1;
+    int64_t so1, sm1;
+    int n1;
+    const float* po2;
+    const float* ml2;
+    int64_t so2, sm2;
+    int n2;
+    __device__ __forceinline__ const float* ml(int p) const {
+        return p < n1 ? ml1 + p * sm1 : ml2 + (p - n1) * sm2;
+    }
+    __device__ __forceinline__ const float* po(int p) const {
+        return p < n1 ? po1 + p * so1 : po2 + (p - n1) * so2;
+    }
+};
+
 template <int V>
-__device__ __forceinline__ void merge_row(const float* __restrict__ po, int64_t so,
-                                          const float* __restrict__ ml, int64_t sm, int np,
-                                          bool row_bad, int c0, void* out_row,
-                                          int32_t out_dtype, float* wsh, float* red,
-                                          f32x4* acc_sh) {
+__device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int c0,
+                                          void* out_row, int32_t out_dtype, float* wsh,
+                                          float* red, f32x4* acc_sh) {
     constexpr int SUB = kThreads / V;  // partial subsets
+    const int np = pr.n1 + pr.n2;
     float mloc = -__builtin_inff();
     for (int p = threadIdx.x; p < np; p += kThreads) {
-        const float2 x = *(const float2*)(ml + p * sm);
+        const float2 x = *(const float2*)pr.ml(p);
         if (x.y != 0.0f) mloc = fmaxf(mloc, x.x);
     }
     const float M = block_max(mloc, red);
     float lsum = 0.0f;
     for (int p = threadIdx.x; p < np; p += kThreads) {
-        const float2 x = *(const float2*)(ml + p * sm);
+        const float2 x = *(const float2*)pr.ml(p);
         const float w = x.y == 0.0f ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
         wsh[p] = w;
         lsum += w;
@@ -74,7 +91,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ po, int64_t 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
     for (int p = sub; p < np; p += SUB) {
-        const f32x4 o = *((const f32x4*)(po + p * so) + c0 + c);
+        const f32x4 o = *((const f32x4*)pr.po(p) + c0 + c);
         const float w = wsh[p];
         if (w != 0.0f) acc += w * o;
     }
@@ -125,38 +142,51 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
         np = min(P, (nblk + bpp - 1) / bpp);
     }
     char* orow = (char*)out + row * HD * (out_dtype == DT_F32 ? 4 : 2);
-    merge_row<HD / 4>(part_o + row * (int64_t)P * HD, HD, part_ml + row * (int64_t)P * 2, 2, np,
-                      row_bad, 0, orow, out_dtype, wsh, red, acc_sh);
+    const PieceRuns pr{part_o + row * (int64_t)P * HD, part_ml + row * (int64_t)P * 2, HD, 2, np,
+                       nullptr, nullptr, 0, 0, 0};
+    merge_row<HD / 4>(pr, row_bad, 0, orow, out_dtype, wsh, red, acc_sh);
 }
 
 // Stream layout (attention kernel's split mode): output row r = seg * g + hh
 // of segment seg; the pieces of a split segment sit in slots seg + w for the
 // waves w in seg_info[seg] = (first, last), piece row (seg + w) * g + hh.
 // Segments with a single piece (written by the attention kernel directly)
-// or none (zero / NaN rows, also written there) are skipped. With CS > 1
-// workgroups per row (grid.y), workgroup (row, cs) handles the cs-th of CS
-// column ranges, so rows with many pieces are spread over several compute
-// units. The weights live in dynamic LDS sized for the wave count.
+// or none (zero / NaN rows, also written there) are skipped. With a shared
+// prefix (prefix_lens != nullptr), a row whose prefix has p blocks also has
+// the prefix pass's pieces of chunks 0 .. ceil(p / kPrefixChunk) - 1, at row
+// c * rows + r of pre_o / pre_ml, and its stream pieces always come here.
+// With CS > 1 workgroups per row (grid.y), workgroup (row, cs) handles the
+// cs-th of CS column ranges, so rows with many pieces are spread over
+// several compute units. The weights live in dynamic LDS sized for the wave
+// count plus the prefix chunks.
 template <int HD, int CS>
-__global__ void __launch_bounds__(kThreads) k_merge_stream(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml,
-                                                           const int2* __restrict__ seg_info,
-                                                           int32_t g, void* out,
-                                                           int32_t out_dtype) {
+__global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
     constexpr int V = HD / 4 / CS;
     extern __shared__ float wsh[];
     __shared__ float red[4];
     __shared__ f32x4 acc_sh[kThreads];
     const int64_t row = blockIdx.x;
+    const int g = a.g;
     const int64_t seg = row / g;
     const int hh = (int)(row - seg * g);
-    const int2 info = seg_info[seg];
+    const int2 info = a.seg_info[seg];
     const int np = info.y - info.x + 1;
-    if (np <= 1) return;
+    int npre = 0;
+    if (a.prefix_lens != nullptr) {
+        const int b = (int)(row / a.n_q);
+        const int pl = row_prefix_len(a.context_lens[b], a.prefix_lens[b], a.max_blocks,
+                                      a.prefix_blocks);
+        npre = pl > 0 ? (pl + kPrefixChunk - 1) / kPrefixChunk : 0;
+    }
+    if (npre == 0 && np <= 1) return;
     const int64_t prow0 = (seg + info.x) * g + hh;
-    char* orow = (char*)out + row * HD * (out_dtype == DT_F32 ? 4 : 2);
-    merge_row<V>(part_o + prow0 * HD, (int64_t)g * HD, part_ml + prow0 * 2, (int64_t)g * 2, np,
-                 false, (int)blockIdx.y * V, orow, out_dtype, wsh, red, acc_sh);
+    const int64_t rows = (int64_t)a.B * a.n_q;
+    char* orow = (char*)a.out + row * HD * (a.out_dtype == DT_F32 ? 4 : 2);
+    const PieceRuns pr{a.part_o + prow0 * HD, a.part_ml + prow0 * 2, (int64_t)g * HD,
+                       (int64_t)g * 2, max(np, 0),
+                       npre ? a.pre_o + row * HD : nullptr, npre ? a.pre_ml + row * 2 : nullptr,
+                       rows * HD, rows * 2, npre};
+    merge_row<V>(pr, false, (int)blockIdx.y * V, orow, a.out_dtype, wsh, red, acc_sh);
 }
 
 hipError_t launch_merge(const float* part_o, const float* part_ml, const int32_t* context_lens,
@@ -182,13 +212,13 @@ hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.n_q;
     if (rows == 0) return hipSuccess;
-    const size_t lds = (size_t)a.nw * sizeof(float);
+    const int chunks = (a.prefix_blocks + kPrefixChunk - 1) / kPrefixChunk;
+    const size_t lds = (size_t)(a.nw + chunks) * sizeof(float);
     // split a row's columns over several workgroups only when segments
     // average many pieces (long sequences in a small batch)
     const bool wide = (int64_t)a.nw >= 64 * (int64_t)a.B * a.n_kv;
 #define PDA_MS(HD, CS)                                                                       \
-    hipLaunchKernelGGL((k_merge_stream<HD, CS>), dim3(rows, CS), dim3(kThreads), lds, s,    \
-                       a.part_o, a.part_ml, a.seg_info, a.g, a.out, a.out_dtype)
+    hipLaunchKernelGGL((k_merge_stream<HD, CS>), dim3(rows, CS), dim3(kThreads), lds, s, a)
     if (a.d_h == 128) {
         if (wide) PDA_MS(128, kMergeColumnSplit);
         else PDA_MS(128, 1);

@@ -28,7 +28,7 @@ Plan make_plan(const pda_attn_desc& d);
 
 // Workspace layout for a plan.
 struct WsLayout {
-    size_t part_o_off, part_ml_off, seg_info_off, bytes;
+    size_t part_o_off, part_ml_off, seg_info_off, pre_o_off, pre_ml_off, bytes;
 };
 WsLayout ws_layout(const pda_attn_desc& d, const Plan& p);
 
@@ -63,6 +63,7 @@ struct AttnArgs {
     int32_t kv_dtype, q_dtype, out_dtype;
     int32_t P, bpp;
     int32_t nw, split;
+    int32_t seg_cost;       // stream split: extra units per non-empty segment
     int32_t reuse_blocks;   // leading logical blocks read with cache-retaining loads
     int32_t window, sinks;  // sliding window (0 = all positions) and its sink tokens
     // fused decode step: the new rows [B][n_kv][d_h] of new_dtype, written into
@@ -70,8 +71,17 @@ struct AttnArgs {
     const void* k_new;
     const void* v_new;
     int32_t new_dtype;
+    // shared prefix (nullptr / 0: none): logical blocks i < prefix_lens[b] of
+    // row b are prefix_table[i]; the prefix pass writes one partial per
+    // (chunk of kPrefixChunk prefix blocks, output row) to pre_o / pre_ml
+    const int32_t* prefix_table;
+    const int32_t* prefix_lens;
+    int32_t prefix_blocks;
+    float* pre_o;    // [chunks][B * n_q][d_h]
+    float* pre_ml;   // [chunks][B * n_q][2]
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s);
 size_t attn_mfma_dyn_lds(int32_t B);
@@ -83,5 +93,7 @@ constexpr int kMaxPartitions = 2048;
 constexpr int kMaxStreamBatch = 4096;      // sequences per call on the stream plan (LDS prefix)
 constexpr int kMaxStreamWaves = 8192;      // wave ranges on the stream plan (merge LDS)
 constexpr int kAttnThreads = 256;
+constexpr int kPrefixChunk = 16;           // shared-prefix blocks per prefix-pass workgroup
+constexpr int kMaxPrefixBlocks = 32768;    // shared-prefix blocks per call (merge LDS)
 
 }  // namespace pda

@@ -209,12 +209,16 @@ typedef struct pda_attn_desc {
     int32_t sink_tokens;        /* attention sinks kept with a window (ignored if window == 0) */
     int32_t new_dtype;          /* pda_decode_step*: pda_dtype of k_new / v_new (PDA_F32 or
                                    PDA_BF16; equal to kv_dtype for 16/32-bit caches) */
+    int32_t prefix_blocks;      /* *_prefix calls: entries of prefix_table (the longest
+                                   shared prefix, in blocks, <= max_blocks_per_seq); sizes
+                                   the workspace. Must be 0 for every other call. */
 } pda_attn_desc;
 
-/* Workspace bytes pda_paged_decode_attn needs for this descriptor (0 when it
- * runs unsplit). Host-only. Layout of a non-empty workspace, 256-B aligned
- * parts: partial outputs float [B][n_q][P][d_h], then partial statistics
- * float [B][n_q][P][2] = (m, l) as defined for pda_lse_merge. */
+/* Workspace bytes the attention calls need for this descriptor (0 when the
+ * call runs unsplit and without a shared prefix). The workspace holds the
+ * split-KV partial results (normalised output, max, sum per piece) and the
+ * split bookkeeping; its layout is internal to the library and nothing in
+ * it needs clearing between calls. Host-only. */
 int32_t pda_attn_workspace_size(const pda_attn_desc* d, size_t* bytes);
 
 /* The split chosen for this descriptor: *num_partitions = P (1 = unsplit) and
@@ -295,6 +299,51 @@ int32_t pda_decode_step_quant(const void* q, const void* k_new, const void* v_ne
                               const int32_t* context_lens, float scale, void* out,
                               const pda_attn_desc* d, void* workspace, size_t ws_bytes,
                               void* stream);
+
+/* Paged decode attention with a shared prefix read once  [SoK paper
+ * section 2.6: prefix sharing stores a prompt prefix's KV state once for
+ * every request that shares it; section 2.5: shared blocks are copy on
+ * write]. Many rows start with the same physical blocks (a system prompt);
+ * instead of every row reading them, one pass reads each shared block once
+ * and applies it to the queries of all rows that share it, the rest of each
+ * row is streamed as in pda_paged_decode_attn, and the partial results are
+ * merged by log-sum-exp. The result is the attention of each row over all its
+ * positions, as pda_paged_decode_attn(_quant) defines it, where logical block
+ * i of row b is
+ *   prefix_table[i]          for i < prefix_lens[b]
+ *   block_table[b][i]        otherwise
+ * (block_table[b][i] is never read for i < prefix_lens[b]).
+ *   k_scale, v_scale   device [num_blocks][n_kv] fp32 for kv_dtype FP8_E4M3 /
+ *                      INT8 (as in pda_paged_decode_attn_quant); NULL for BF16
+ *   prefix_table       device int32 [d->prefix_blocks], physical block ids
+ *   prefix_lens        device int32 [B], shared-prefix blocks of each row
+ * kv_dtype BF16, FP8_E4M3 or INT8; window must be 0; d->prefix_blocks > 0.
+ * A row with n > 0 needs 0 <= prefix_lens[b] <= min(prefix_blocks,
+ * ceil(n / bs) - 1): the block holding its newest position is its own (copy
+ * on write); otherwise, or with an unmapped prefix_table entry among its
+ * first prefix_lens[b], the row's output is NaN. Rows with n == 0 are zero
+ * (prefix_lens ignored). Other arguments, errors and the workspace
+ * (pda_attn_workspace_size of the same descriptor) as for
+ * pda_paged_decode_attn. */
+int32_t pda_paged_decode_attn_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     const int32_t* prefix_table, const int32_t* prefix_lens,
+                                     float scale, void* out, const pda_attn_desc* d,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Fused decode step with a shared prefix read once: each row's new token is
+ * written to position n - 1 (as pda_decode_step / pda_decode_step_quant
+ * write it; that block is never a prefix block) and the row is then attended
+ * as in pda_paged_decode_attn_prefix. The caches end bit for bit as after
+ * pda_kv_append(_quant). */
+int32_t pda_decode_step_prefix(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, const float* k_scale,
+                               const float* v_scale, const int32_t* block_table,
+                               const int32_t* context_lens, const int32_t* prefix_table,
+                               const int32_t* prefix_lens, float scale, void* out,
+                               const pda_attn_desc* d, void* workspace, size_t ws_bytes,
+                               void* stream);
 
 /* Log-sum-exp merge of split-KV partial results. For each of `rows` rows and
  * P partials with (o_p, m_p, l_p):

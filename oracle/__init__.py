@@ -29,6 +29,10 @@ Contents, each written from the pages' statement of the method:
                        fp8 is OCP E4M3; the quantizer picks the nearest finite
                        code by brute force with ties to the even code.
 * `merge`           -- log-sum-exp merge of split-KV partial results.
+* `prefix_block_table`, `prefix_row_len` -- a prompt prefix stored once and
+                       shared by many rows (SoK paper section 2.6): the block
+                       table a shared-prefix call attends through, and which
+                       rows are valid (copy on write, section 2.5).
 * `OraclePool`      -- fixed-size blocks allocated on demand from a free list,
                        per-request block tables, reference-counted sharing
                        with copy-on-write (section 9.5; SoK section 2.5, tau=16).
@@ -161,6 +165,42 @@ def merge(o: np.ndarray, m: np.ndarray, z: np.ndarray) -> np.ndarray:
     M = m[live].max()
     w = np.where(live, z * np.exp(np.where(live, m, M) - M), 0.0)
     return (w[:, None] * np.where(live[:, None], o, 0.0)).sum(axis=0) / w.sum()
+
+
+# ------------------------------------------------------------ shared prefix
+def prefix_row_len(n: int, pl: int, max_blocks: int, prefix_blocks: int) -> int:
+    """Shared-prefix length of one row, or -1 for an invalid row. A row's first
+    pl logical blocks are the shared prefix's blocks (SoK paper section 2.6,
+    prefix sharing); the block that receives the row's newest token is never
+    shared (section 2.5, copy on write), so pl <= ceil(n / bs) - 1, and pl
+    cannot exceed the prefix table. An empty row has no prefix; a row whose
+    length is itself invalid is invalid."""
+    if n < 0 or n > max_blocks * 16:
+        return -1
+    if n == 0:
+        return 0
+    if pl < 0 or pl > prefix_blocks or pl >= (n + 15) // 16:
+        return -1
+    return pl
+
+
+def prefix_block_table(block_table, context_lens, prefix_table, prefix_lens):
+    """The block table a shared-prefix call attends through: logical block i
+    of row b is prefix_table[i] for i < prefix_lens[b], else block_table[b][i].
+    Returns (table [B, max_blocks] int32, invalid [B] bool); an invalid row
+    (see prefix_row_len) keeps its entries and must come out NaN."""
+    table = np.array(block_table, dtype=np.int32, copy=True)
+    B, max_blocks = table.shape
+    pt = [int(x) for x in prefix_table]
+    invalid = np.zeros(B, dtype=bool)
+    for b in range(B):
+        pl = prefix_row_len(int(context_lens[b]), int(prefix_lens[b]), max_blocks, len(pt))
+        if pl < 0:
+            invalid[b] = True
+            continue
+        for i in range(pl):
+            table[b, i] = pt[i]
+    return table, invalid
 
 
 # ---------------------------------------------------------- lookup and append

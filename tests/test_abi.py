@@ -49,7 +49,7 @@ def _desc(**kw):
     base = dict(B=2, n_q=8, n_kv=2, d_h=128, block_size=16, max_blocks_per_seq=64,
                 num_blocks=200, kv_dtype=pda.BF16, q_dtype=pda.BF16, out_dtype=pda.F32,
                 max_context=1000, num_partitions=0, total_context=0, reuse_prefix_blocks=0,
-                window=0, sink_tokens=0, new_dtype=pda.BF16)
+                window=0, sink_tokens=0, new_dtype=pda.BF16, prefix_blocks=0)
     base.update(kw)
     return pda.AttnDesc(*[base[f] for f, _ in pda.AttnDesc._fields_])
 
@@ -60,7 +60,10 @@ def _desc(**kw):
                                  dict(max_blocks_per_seq=0), dict(num_blocks=0),
                                  dict(max_context=-1), dict(B=-1),
                                  dict(reuse_prefix_blocks=-1),
-                                 dict(window=-1), dict(sink_tokens=-1)])
+                                 dict(window=-1), dict(sink_tokens=-1),
+                                 dict(prefix_blocks=-1), dict(prefix_blocks=65),
+                                 dict(prefix_blocks=4, window=64),
+                                 dict(prefix_blocks=4, kv_dtype=pda.F32)])
 def test_attention_descriptor_validation(bad):
     with pytest.raises(pda.PdaError):
         pda.attn_workspace_size(_desc(**bad))
@@ -133,3 +136,61 @@ def test_null_pointers_rejected_without_gpu():
     assert binding._lib.pda_lse_merge(None, None, 4, 0, 128, None, None) == binding.EINVAL
     assert binding._lib.pda_lse_merge(None, None, 4, 2049, 128, None, None) == binding.EINVAL
     assert binding._lib.pda_lse_merge(None, None, 0, 4, 128, None, None) == binding.OK
+
+
+def _ws_parts(d):
+    """Expected stream-plan workspace bytes: partial slots, their statistics,
+    segment info, and (with a shared prefix) the prefix pass's partials."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    P, _ = pda.attn_plan(d)
+    S, g, rows = d.B * d.n_kv, d.n_q // d.n_kv, d.B * d.n_q
+    n = a256((S + P) * g * d.d_h * 4) + a256((S + P) * g * 2 * 4) + a256(S * 8)
+    if d.prefix_blocks:
+        chunks = -(-d.prefix_blocks // 16)
+        n += a256(chunks * rows * d.d_h * 4) + a256(chunks * rows * 2 * 4)
+    return n
+
+
+def test_prefix_plan_and_workspace():
+    # a shared prefix always takes the split plan (the suffix pieces go through
+    # the merge), even where the plain call would run unsplit
+    d = _desc(B=64, n_q=32, n_kv=8, max_blocks_per_seq=4, max_context=40, total_context=64 * 40)
+    assert pda.attn_plan(d)[0] == 1 and pda.attn_workspace_size(d) == 0
+    d.prefix_blocks = 2
+    P, _ = pda.attn_plan(d)
+    assert P == 64 * 8   # "unsplit": one range per (sequence, KV head)
+    assert pda.attn_workspace_size(d) == _ws_parts(d)
+    # shared-prefix workload shape: 128 prefix blocks -> 8 chunks of 16
+    d = _desc(B=64, n_q=32, n_kv=8, max_blocks_per_seq=1024, num_blocks=40000,
+              max_context=16384, total_context=64 * 8704, kv_dtype=pda.FP8_E4M3,
+              prefix_blocks=128)
+    assert pda.attn_workspace_size(d) == _ws_parts(d)
+    plain = _desc(B=64, n_q=32, n_kv=8, max_blocks_per_seq=1024, num_blocks=40000,
+                  max_context=16384, total_context=64 * 8704, kv_dtype=pda.FP8_E4M3)
+    assert pda.attn_plan(plain) == pda.attn_plan(d)
+    assert pda.attn_workspace_size(d) - pda.attn_workspace_size(plain) == \
+        8 * 64 * 32 * 128 * 4 + 8 * 64 * 32 * 2 * 4
+    with pytest.raises(pda.PdaError):   # beyond the per-call prefix limit
+        pda.attn_workspace_size(_desc(max_blocks_per_seq=40000, prefix_blocks=32769))
+
+
+def test_prefix_calls_check_the_descriptor_first():
+    null13 = (None,) * 9
+    d0 = _desc()                       # prefix_blocks == 0: not a shared-prefix call
+    rc = binding._lib.pda_paged_decode_attn_prefix(*null13, 1.0, None,
+                                                   binding.ctypes.byref(d0), None, 0, None)
+    assert rc == binding.EINVAL and "prefix_blocks" in pda.last_error()
+    d4 = _desc(prefix_blocks=4)        # the plain calls refuse a prefix descriptor
+    rc = binding._lib.pda_paged_decode_attn(None, None, None, None, None, 1.0, None,
+                                            binding.ctypes.byref(d4), None, 0, None)
+    assert rc == binding.EINVAL and "prefix" in pda.last_error()
+    rc = binding._lib.pda_decode_step_prefix(*((None,) * 11), 1.0, None,
+                                             binding.ctypes.byref(_desc(prefix_blocks=4,
+                                                                        kv_dtype=pda.F32)),
+                                             None, 0, None)
+    assert rc == binding.EINVAL
+    # valid descriptor, NULL prefix pointers
+    rc = binding._lib.pda_paged_decode_attn_prefix(*null13, 1.0, None,
+                                                   binding.ctypes.byref(d4), None, 0, None)
+    assert rc == binding.EINVAL and "NULL" in pda.last_error()

@@ -24,7 +24,10 @@ from tests.gpu_helpers import TOL_16BIT, TOL_8BIT
 pytestmark = pytest.mark.gpu
 
 FULL = ["tiny_mha", "llama3_8b_layer", "llama3_70b_layer_b8_32k", "long_context_131k_sinks",
-        "quant_prefix_fp8", "quant_prefix_int8", "llama3_70b_layer_b8_32k_window4k_sinks4"]
+        "quant_prefix_fp8", "quant_prefix_int8", "llama3_70b_layer_b8_32k_window4k_sinks4",
+        # the shared-prefix workloads again through the fused shared-prefix step
+        # (each shared block read once), the benchmark's launch for them
+        "quant_prefix_fp8:prefix", "quant_prefix_int8:prefix"]
 
 
 def _raw(t):
@@ -49,7 +52,9 @@ def test_full_size_workload(name):
     import torch
     import decode_attention_paged_slot_amd as pda
 
-    w = synth.WORKLOADS[name]
+    wname, _, mode = name.partition(":")
+    w = synth.WORKLOADS[wname]
+    cascade = mode == "prefix"
     print(f"full-size parity: {name}", flush=True)
     sys.stdout.flush()
     dev = "cuda"
@@ -86,13 +91,27 @@ def test_full_size_workload(name):
                          kv_dtype=w.kv_dtype, total_context=int(inp.ctx.sum()),
                          reuse_prefix_blocks=w.shared_prefix_tokens // w.block_size,
                          window=w.attn_window, sink_tokens=w.attn_sinks)
-    ws = pda.workspace_for(desc, dev)
-    if quant:
+    if cascade:
+        n_sh = inp.shared_ids_count
+        nblk = synth.blocks_needed(inp.ctx, bs)
+        plen = np.minimum(n_sh, np.maximum(nblk - 1, 0)).astype(np.int32)
+        desc.prefix_blocks = n_sh
+        desc.reuse_prefix_blocks = 0
+        desc.new_dtype = synth.BF16
+        ws = pda.workspace_for(desc, dev)
+        pt = torch.from_numpy(np.asarray(osh, dtype=np.int32)).to(dev)
+        pls = torch.from_numpy(plen).to(dev)
+        pda.decode_step_prefix(inp.q, inp.k_new, inp.v_new, inp.k_cache, inp.v_cache,
+                               inp.k_scale, inp.v_scale, bt, cl, pt, pls, w.softmax_scale, out,
+                               desc=desc, workspace=ws)
+    elif quant:
+        ws = pda.workspace_for(desc, dev)
         pda.kv_append_quant(inp.k_new, inp.v_new, sl, inp.k_cache, inp.v_cache, inp.k_scale,
                             inp.v_scale, cache_dtype=w.kv_dtype)
         pda.paged_decode_attn_quant(inp.q, inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale,
                                     bt, cl, w.softmax_scale, out, desc=desc, workspace=ws)
     else:
+        ws = pda.workspace_for(desc, dev)
         pda.kv_append(inp.k_new, inp.v_new, sl, inp.k_cache, inp.v_cache)
         pda.paged_decode_attn(inp.q, inp.k_cache, inp.v_cache, bt, cl, w.softmax_scale, out,
                               desc=desc, workspace=ws)

@@ -380,6 +380,45 @@ def test_prefix_aliasing_bit_identical():
     assert (shared == private).all()
 
 
+def test_prefix_block_table_worked_case():
+    """Shared-prefix table (SoK paper section 2.6; copy on write, section 2.5):
+    rows' first prefix_lens[b] logical blocks come from the prefix table,
+    using the worked example's physical blocks 7, 2, 15 as the prefix."""
+    bt = np.array([[-1, -1, 40, 41, -1],
+                   [50, 51, 52, -1, -1],
+                   [-1, -1, -1, 60, -1]], dtype=np.int32)
+    table, bad = oracle.prefix_block_table(bt, [64, 40, 50], [7, 2, 15], [2, 0, 3])
+    assert table.tolist() == [[7, 2, 40, 41, -1], [50, 51, 52, -1, -1], [7, 2, 15, 60, -1]]
+    assert not bad.any()
+    # validity: the newest token's block is private, the prefix fits its table
+    L = oracle.prefix_row_len
+    assert L(64, 3, 5, 3) == 3 and L(64, 4, 5, 4) == -1      # 4 blocks: at most 3 shared
+    assert L(49, 3, 5, 3) == 3 and L(48, 3, 5, 3) == -1      # 48 tokens fill 3 blocks
+    assert L(64, 3, 5, 2) == -1 and L(64, -1, 5, 3) == -1
+    assert L(0, 7, 5, 3) == 0                                # empty row: no prefix
+    assert L(-1, 0, 5, 3) == -1 and L(81, 0, 5, 3) == -1     # invalid lengths
+    _, bad = oracle.prefix_block_table(bt, [64, 32, 50], [7, 2, 15], [2, 2, 3])
+    assert bad.tolist() == [False, True, False]
+
+
+def test_prefix_block_table_matches_the_cow_builder():
+    """The copy-on-write builder shares min(n_shared, blocks - 1) leading
+    blocks per row; the prefix table with those lengths reproduces its table,
+    also where the rows' own entries for the prefix were never filled."""
+    pool = oracle.OraclePool(64, list(np.random.default_rng(3).permutation(64)))
+    shared = pool.alloc(5)
+    ctx = [100, 16, 17, 80, 0, 1, 65]
+    table, _ = pool.build_block_table(ctx, 16, 8, shared)
+    lens = [min(5, max((n + 15) // 16 - 1, 0)) for n in ctx]
+    eff, bad = oracle.prefix_block_table(table, ctx, shared, lens)
+    assert (eff == table).all() and not bad.any()
+    blank = table.copy()
+    for b, pl in enumerate(lens):
+        blank[b, :pl] = -1
+    eff, bad = oracle.prefix_block_table(blank, ctx, shared, lens)
+    assert (eff == table).all() and not bad.any()
+
+
 def test_matches_torch_sdpa_fp64():
     """torch's fp64 scaled_dot_product_attention (a library routine) on the
     gathered contiguous sequence, with GQA."""
