@@ -33,6 +33,11 @@ Contents, each written from the pages' statement of the method:
                        shared by many rows (SoK paper section 2.6): the block
                        table a shared-prefix call attends through, and which
                        rows are valid (copy on write, section 2.5).
+* `int4` (module)   -- 4-bit cache with per-channel key scales, per-token
+                       value scales and a full-precision residual window
+                       (SoK paper sections 2.3 and 4.3): format, quantizer,
+                       append policy, decoded cache; `paged_attn_int4`
+                       attends through it.
 * `OraclePool`      -- fixed-size blocks allocated on demand from a free list,
                        per-request block tables, reference-counted sharing
                        with copy-on-write (section 9.5; SoK section 2.5, tau=16).
@@ -150,6 +155,17 @@ def paged_attn(q, k_cache, v_cache, block_table, context_lens, scale, *, n_q, n_
     if bad < 0:
         raise ValueError("oracle: bad arguments")
     return out, m, z, int(bad)
+
+
+def paged_attn_int4(q, state: dict, k_scale, block_table, context_lens, scale, *, n_q, n_kv,
+                    q_dtype, rows=None, nthreads=0):
+    """Decode attention over a 4-bit cache with a residual window: the
+    definition of paged_attn applied to the cache as stored (full blocks
+    decoded, each row's open block from its residual buffer; see int4)."""
+    from . import int4
+    k64, v64, table = int4.decoded_cache(state, k_scale, block_table, context_lens)
+    return paged_attn(q, k64, v64, table, context_lens, scale, n_q=n_q, n_kv=n_kv,
+                      q_dtype=q_dtype, kv_dtype=int4.F64, rows=rows, nthreads=nthreads)
 
 
 def merge(o: np.ndarray, m: np.ndarray, z: np.ndarray) -> np.ndarray:

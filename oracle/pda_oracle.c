@@ -57,7 +57,9 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_INT8 = 3 };
+/* cache element formats; OR_F64 holds values already decoded to fp64 (the
+ * 4-bit cache is decoded on the Python side, see oracle/__init__.py) */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_INT8 = 3, OR_F64 = 5 };
 
 static double or_dec_f32(const void* p, int64_t i) {
     float f;
@@ -91,6 +93,12 @@ static double or_dec_int8(const void* p, int64_t i) {
     return (double)((const int8_t*)p)[i];
 }
 
+static double or_dec_f64(const void* p, int64_t i) {
+    double d;
+    memcpy(&d, (const char*)p + 8 * i, 8);
+    return d;
+}
+
 typedef double (*or_dec_fn)(const void*, int64_t);
 
 /* Is logical position t of an n-token row attended (window / sink rule)? */
@@ -104,6 +112,7 @@ static or_dec_fn or_decoder(int dtype) {
     case OR_BF16: return or_dec_bf16;
     case OR_FP8: return or_dec_fp8;
     case OR_INT8: return or_dec_int8;
+    case OR_F64: return or_dec_f64;
     default: return NULL;
     }
 }
