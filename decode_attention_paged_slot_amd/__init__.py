@@ -14,12 +14,13 @@ import importlib
 
 _BINDING_NAMES = (
     "AttnDesc", "KvDesc", "NoSpace", "PdaError", "Pool", "EXPORTS", "LIB_PATH",
-    "F32", "BF16", "FP8_E4M3", "INT8",
+    "F32", "BF16", "FP8_E4M3", "INT8", "INT4",
     "version", "last_error", "dtype_code",
     "kv_append", "kv_append_quant",
     "attn_desc", "attn_workspace_size", "attn_plan", "workspace_for",
     "paged_decode_attn", "paged_decode_attn_quant", "lse_merge",
     "decode_step", "decode_step_quant", "paged_decode_attn_prefix", "decode_step_prefix",
+    "kv_append_int4", "paged_decode_attn_int4",
 )
 
 __all__ = list(_BINDING_NAMES)

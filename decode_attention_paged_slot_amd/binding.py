@@ -33,7 +33,7 @@ except ImportError:
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, EINVAL, ENOSPC, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
-F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, INT8, INT4 = 0, 1, 2, 3, 4
 _STATUS = {EINVAL: "EINVAL", ENOSPC: "ENOSPC", EWORKSPACE: "EWORKSPACE", EHIP: "EHIP"}
 
 
@@ -98,6 +98,11 @@ _SIGS = {
     "pda_decode_step_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_float, _vp, ctypes.POINTER(AttnDesc), _vp, _sz,
                                       _vp]),
+    "pda_kv_append_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.POINTER(AttnDesc), _vp]),
+    "pda_paged_decode_attn_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.c_float, _vp, ctypes.POINTER(AttnDesc), _vp,
+                                          _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -314,6 +319,34 @@ def decode_step_prefix(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, bloc
                                        _ptr(prefix_lens), float(scale), _ptr(out),
                                        ctypes.byref(desc), _ptr(workspace), ws_bytes,
                                        _stream(stream)), "pda_decode_step_prefix")
+
+
+def kv_append_int4(k_new, v_new, block_table, context_lens, k_q, v_q, k_scale, v_scale, k_res,
+                   v_res, *, desc: AttnDesc, stream=None) -> None:
+    """pda_kv_append_int4: each row's newest token into its residual slot;
+    a filled block is encoded into the 4-bit cache. k_new, v_new [B, n_kv,
+    d_h] bf16; k_q, v_q [NB, n_kv, 16, d_h / 2] uint8; k_scale [n_kv, d_h]
+    f32; v_scale [NB, n_kv, 16] f32; k_res, v_res [B, n_kv, 16, d_h] bf16."""
+    _check(_lib.pda_kv_append_int4(_ptr(k_new), _ptr(v_new), _ptr(block_table),
+                                   _ptr(context_lens), _ptr(k_q), _ptr(v_q), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(k_res), _ptr(v_res), ctypes.byref(desc),
+                                   _stream(stream)), "pda_kv_append_int4")
+
+
+def paged_decode_attn_int4(q, k_q, v_q, k_scale, v_scale, k_res, v_res, block_table,
+                           context_lens, scale: float, out, *, desc: AttnDesc, workspace=None,
+                           stream=None) -> None:
+    """pda_paged_decode_attn_int4: attention over the 4-bit cache and the
+    rows' residual windows (desc.kv_dtype = INT4)."""
+    if workspace is None:
+        workspace = workspace_for(desc, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pda_paged_decode_attn_int4(_ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scale),
+                                           _ptr(v_scale), _ptr(k_res), _ptr(v_res),
+                                           _ptr(block_table), _ptr(context_lens), float(scale),
+                                           _ptr(out), ctypes.byref(desc), _ptr(workspace),
+                                           ws_bytes, _stream(stream)),
+           "pda_paged_decode_attn_int4")
 
 
 def lse_merge(part_o, part_ml, out, *, stream=None) -> None:

@@ -97,8 +97,9 @@ Plan make_stream_plan(const pda_attn_desc& d) {
     const int64_t t_est = (int64_t)d.n_kv *
         (d.total_context > 0 ? ceil_div(d.total_context, d.block_size) + d.B : d.B * nblk_max);
     Plan p{1, (int32_t)std::max<int64_t>(nblk_max, 1), (int32_t)S, 0, 1};
-    if (d.prefix_blocks > 0) {
-        // with a shared prefix every row's suffix goes through the merge, so
+    if (d.prefix_blocks > 0 || d.kv_dtype == PDA_INT4) {
+        // with a shared prefix (or a 4-bit cache's residual window) every
+        // row's pieces go through the merge, so
         // the split bookkeeping is always on; "unsplit" is one range per segment
         Plan q = p;
         if (d.num_partitions != 1) q = make_stream_plan_split(d, S, t_est);
@@ -125,7 +126,8 @@ Plan make_stream_plan_split(const pda_attn_desc& d, int64_t S, int64_t t_est) {
     } else {
         // 8-bit caches do twice the conversion and matrix work per byte and
         // need two workgroups per compute unit to keep HBM busy
-        const bool eight_bit = d.kv_dtype == PDA_FP8_E4M3 || d.kv_dtype == PDA_INT8;
+        const bool eight_bit = d.kv_dtype == PDA_FP8_E4M3 || d.kv_dtype == PDA_INT8 ||
+                               d.kv_dtype == PDA_INT4;
         const int64_t wgs = std::max(env_int("PDA_ATTN_WORKGROUPS", eight_bit ? 512 : 256), 1);
         const int64_t min_blocks = std::max(env_int("PDA_MIN_BLOCKS_PER_WAVE", 8), 1);
         nw = std::min<int64_t>(4 * wgs, (t_est + min_blocks - 1) / min_blocks);
@@ -155,8 +157,10 @@ WsLayout ws_layout(const pda_attn_desc& d, const Plan& p) {
         w.part_ml_off = align256(slots * g * d.d_h * sizeof(float));
         w.seg_info_off = w.part_ml_off + align256(slots * g * 2 * sizeof(float));
         w.bytes = w.seg_info_off + align256(S * 2 * sizeof(int32_t));
-        if (d.prefix_blocks > 0) {
-            const size_t chunks = (size_t)ceil_div(d.prefix_blocks, kPrefixChunk);
+        if (d.prefix_blocks > 0 || d.kv_dtype == PDA_INT4) {
+            // prefix pass pieces, or the 4-bit cache's residual-window piece
+            const size_t chunks =
+                d.prefix_blocks > 0 ? (size_t)ceil_div(d.prefix_blocks, kPrefixChunk) : 1;
             const size_t rows = (size_t)d.B * d.n_q;
             w.pre_o_off = w.bytes;
             w.pre_ml_off = w.pre_o_off + align256(chunks * rows * d.d_h * sizeof(float));
@@ -179,7 +183,7 @@ using namespace pda;
 namespace {
 
 // Which call a descriptor is checked for.
-enum CallKind { kPlain, kQuant, kPrefix, kQuery };
+enum CallKind { kPlain, kQuant, kPrefix, kInt4, kQuery };
 
 int32_t check_attn_desc(const pda_attn_desc* d, CallKind kind) {
     if (!d) {
@@ -212,10 +216,12 @@ int32_t check_attn_desc(const pda_attn_desc* d, CallKind kind) {
     }
     const bool eight = d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8;
     const bool wide = d->kv_dtype == PDA_F32 || d->kv_dtype == PDA_BF16;
+    const bool int4 = d->kv_dtype == PDA_INT4;
     const bool kv_ok = kind == kQuant    ? eight
                        : kind == kPlain  ? wide
                        : kind == kPrefix ? (eight || d->kv_dtype == PDA_BF16)
-                                         : (eight || wide);
+                       : kind == kInt4   ? int4
+                                         : (eight || wide || int4);
     if (!kv_ok) {
         set_error("kv_dtype %d not valid for this call", d->kv_dtype);
         return PDA_EINVAL;
@@ -228,6 +234,10 @@ int32_t check_attn_desc(const pda_attn_desc* d, CallKind kind) {
     }
     if (kind == kPrefix && d->prefix_blocks == 0) {
         set_error("shared-prefix call with prefix_blocks == 0");
+        return PDA_EINVAL;
+    }
+    if (int4 && (d->window != 0 || d->prefix_blocks != 0)) {
+        set_error("a 4-bit cache takes no window and no shared prefix");
         return PDA_EINVAL;
     }
     if ((kind == kPlain || kind == kQuant) && d->prefix_blocks != 0) {
@@ -292,10 +302,12 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
                  float scale, void* out, const pda_attn_desc* d, void* workspace,
                  size_t ws_bytes, void* stream, CallKind kind, const void* k_new = nullptr,
                  const void* v_new = nullptr, bool fused = false,
-                 const int32_t* prefix_table = nullptr, const int32_t* prefix_lens = nullptr) {
+                 const int32_t* prefix_table = nullptr, const int32_t* prefix_lens = nullptr,
+                 const void* k_res = nullptr, const void* v_res = nullptr) {
     int32_t rc = check_attn_desc(d, kind);
     if (rc != PDA_OK) return rc;
-    const bool quant = d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8;
+    const bool quant = d->kv_dtype == PDA_FP8_E4M3 || d->kv_dtype == PDA_INT8 ||
+                       d->kv_dtype == PDA_INT4;
     if (fused) {
         const bool ok = quant ? (d->new_dtype == PDA_F32 || d->new_dtype == PDA_BF16)
                               : d->new_dtype == d->kv_dtype;
@@ -311,7 +323,8 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     }
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
         (quant && (!k_scale || !v_scale)) ||
-        (kind == kPrefix && (!prefix_table || !prefix_lens))) {
+        (kind == kPrefix && (!prefix_table || !prefix_lens)) ||
+        (kind == kInt4 && (!k_res || !v_res))) {
         set_error("NULL device pointer");
         return PDA_EINVAL;
     }
@@ -378,8 +391,12 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     a.prefix_table = prefix ? prefix_table : nullptr;
     a.prefix_lens = prefix ? prefix_lens : nullptr;
     a.prefix_blocks = prefix ? d->prefix_blocks : 0;
-    a.pre_o = prefix ? (float*)((char*)workspace + ws.pre_o_off) : nullptr;
-    a.pre_ml = prefix ? (float*)((char*)workspace + ws.pre_ml_off) : nullptr;
+    const bool int4 = kind == kInt4;
+    a.pre_o = prefix || int4 ? (float*)((char*)workspace + ws.pre_o_off) : nullptr;
+    a.pre_ml = prefix || int4 ? (float*)((char*)workspace + ws.pre_ml_off) : nullptr;
+    a.k_res = int4 ? k_res : nullptr;
+    a.v_res = int4 ? v_res : nullptr;
+    a.extra_pieces = int4 ? 1 : 0;
     hipError_t e;
     if (prefix) {
         // the shared blocks first: they are never the block a fused step writes
@@ -389,6 +406,11 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     if (plan.stream) {
         e = launch_attn_mfma(a, s);
         if (e != hipSuccess) return hip_fail("attention launch", e);
+        if (int4) {
+            // the open blocks' residual-window tokens, one piece per row
+            e = launch_attn_residual(a, s);
+            if (e != hipSuccess) return hip_fail("residual attention launch", e);
+        }
         if (plan.split) {
             e = launch_merge_stream(a, s);
             if (e != hipSuccess) return hip_fail("merge launch", e);
@@ -562,6 +584,45 @@ int32_t pda_decode_step_prefix(const void* q, const void* k_new, const void* v_n
     return run_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out,
                     d, workspace, ws_bytes, stream, kPrefix, k_new, v_new, true, prefix_table,
                     prefix_lens);
+}
+
+int32_t pda_paged_decode_attn_int4(const void* q, const void* k_q, const void* v_q,
+                                   const float* k_scale, const float* v_scale,
+                                   const void* k_res, const void* v_res,
+                                   const int32_t* block_table, const int32_t* context_lens,
+                                   float scale, void* out, const pda_attn_desc* d,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+    if ((k_res && !aligned16(k_res)) || (v_res && !aligned16(v_res)) ||
+        (k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale))) {
+        set_error("k_res, v_res, k_scale and v_scale must be 16-byte aligned");
+        return PDA_EINVAL;
+    }
+    return run_attn(q, k_q, v_q, k_scale, v_scale, block_table, context_lens, scale, out, d,
+                    workspace, ws_bytes, stream, kInt4, nullptr, nullptr, false, nullptr, nullptr,
+                    k_res, v_res);
+}
+
+int32_t pda_kv_append_int4(const void* k_new, const void* v_new, const int32_t* block_table,
+                           const int32_t* context_lens, void* k_q, void* v_q,
+                           const float* k_scale, float* v_scale, void* k_res, void* v_res,
+                           const pda_attn_desc* d, void* stream) {
+    int32_t rc = check_attn_desc(d, kInt4);
+    if (rc != PDA_OK) return rc;
+    if (d->B == 0) return PDA_OK;
+    if (!k_new || !v_new || !block_table || !context_lens || !k_q || !v_q || !k_scale ||
+        !v_scale || !k_res || !v_res) {
+        set_error("NULL device pointer");
+        return PDA_EINVAL;
+    }
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_q) || !aligned16(v_q) ||
+        !aligned16(k_res) || !aligned16(v_res) || !aligned16(k_scale) || !aligned16(v_scale)) {
+        set_error("int4 append buffers must be 16-byte aligned");
+        return PDA_EINVAL;
+    }
+    hipError_t e = launch_append_int4(k_new, v_new, block_table, context_lens, k_q, v_q, k_scale,
+                                      v_scale, k_res, v_res, d->B, d->n_kv, d->d_h,
+                                      d->max_blocks_per_seq, d->num_blocks, (hipStream_t)stream);
+    return e == hipSuccess ? PDA_OK : hip_fail("int4 append launch", e);
 }
 
 int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,

@@ -60,10 +60,12 @@ constexpr float kSlack = 8.0f;   // lazy-rescaling threshold (weights < 2^8)
 
 template <int HD, int KV>
 struct Tr {
-    static constexpr int W = (KV == DT_BF16) ? 2 : 1;   // bytes per cached element
-    static constexpr int ROWB = HD * W;                 // bytes per token row
+    static constexpr bool I4 = KV == DT_INT4;
+    static constexpr int W = (KV == DT_BF16) ? 2 : 1;   // bytes per cached element (16/8-bit)
+    static constexpr int ROWB = I4 ? HD / 2 : HD * W;   // bytes per token row
     static constexpr int TILEB = 16 * ROWB;             // bytes per (block, head) tile
-    static constexpr int LOADS = TILEB / 1024;          // 16-B loads per lane per tile
+    static constexpr int LOADS = I4 ? 1 : TILEB / 1024; // 16-B loads per lane per tile
+    static constexpr int LB = TILEB / 64;               // 4-bit: tile bytes per lane (16 or 8)
     static constexpr int NCH = HD / 32;                 // QK k-chunks
     static constexpr int NT = HD / 16;                  // PV output tiles
     static constexpr int LROW = HD * 2;                 // bytes per bf16 LDS row
@@ -76,7 +78,9 @@ struct Tr {
 // First element of QK chunk c held by lane group grp (8 consecutive elements).
 template <int HD, int KV>
 __device__ __forceinline__ constexpr int dmap(int c, int grp) {
-    return KV == DT_BF16 ? 32 * c + 8 * grp : 64 * (c / 2) + 16 * grp + 8 * (c % 2);
+    return KV == DT_BF16   ? 32 * c + 8 * grp
+           : KV == DT_INT4 ? (HD / 4) * grp + 8 * c   // lane group grp: channels of its 16-B load
+                           : 64 * (c / 2) + 16 * grp + 8 * (c % 2);
 }
 
 __device__ __forceinline__ uint4 ld16(const char* p) { return *(const uint4*)p; }
@@ -140,7 +144,8 @@ struct Meta {
 template <int HD, int KV, int QT>
 __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mfma(AttnArgs a) {
     using T = Tr<HD, KV>;
-    constexpr bool QUANT = KV != DT_BF16;
+    constexpr bool QUANT = KV == DT_FP8 || KV == DT_INT8;   // 8-bit, per-(block, head) scales
+    constexpr bool I4 = KV == DT_INT4;   // 4-bit: per-channel K and per-token V scales
     // per wave: the V tile (bf16) and, for bf16 caches, the K tile
     constexpr bool KST = KV == DT_BF16;
     __shared__ __attribute__((aligned(16))) char stage_all[4 * T::LTILE * (KST ? 2 : 1)];
@@ -174,6 +179,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                                ? (n < 0 || n > a.max_blocks * 16 ? -1 : 0)
                                : row_prefix_len(n, a.prefix_lens[b], a.max_blocks,
                                                 a.prefix_blocks);
+            if (I4) return pl < 0 ? -1 : n / 16;   // encoded blocks; the open one is a piece of its own
             return pl < 0 ? -1 : row_blocks(n, a.window, a.sinks).count - pl;
         };
         int local = 0, localu = 0;
@@ -324,7 +330,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             if (id < 0 || id >= a.num_blocks) id = -1;
             const int seg = b * n_kv + j;
             m.id = id;
-            m.info = ((pl > 0) << 4) | ((bl == 0) << 5) | ((bl == nb - 1) << 6) |
+            m.info = ((pl > 0 || a.extra_pieces > 0) << 4) | ((bl == 0) << 5) | ((bl == nb - 1) << 6) |
                      ((blk < a.reuse_blocks) << 7) | (seg << 8);
             m.mask = (int)block_token_mask(blk, nn[b], a.window, a.sinks);
             if (QUANT && id >= 0) {
@@ -338,13 +344,54 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     // ---- query operands (B operand of S^T = K . Q^T): lane (h, grp), for
     // the g query rows of segment `seg` (rows seg * g .. seg * g + g - 1)
     bf16x8 qhi[T::NCH], qlo[T::NCH];
+    // 4-bit: the per-channel key scales are folded into the queries,
+    // q' = q * k_scale[j][:] in fp32, split into bf16 hi + lo; the K operand
+    // holds 136 + code, so every score carries the offset 136 * sum_d q'_d,
+    // which cq removes (computed from the very hi and lo values multiplied)
+    float cq = 0.0f;
     auto load_q = [&](int seg) {
         const bool live = col < g;
         const int64_t qrow = ((int64_t)seg * g + (live ? col : 0)) * HD;
+        float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < T::NCH; ++c) {
             const int d0 = dmap<HD, KV>(c, grp);
-            if (QT == DT_BF16) {
+            if constexpr (I4) {
+                float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (live) {
+                    if (QT == DT_BF16) {
+                        const uint4 w = ld16((const char*)a.q + (qrow + d0) * 2);
+                        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            f[2 * k] = bf16_lo_to_f32(ws[k]);
+                            f[2 * k + 1] = bf16_hi_to_f32(ws[k]);
+                        }
+                    } else {
+                        const float4 x0 = *(const float4*)((const float*)a.q + qrow + d0);
+                        const float4 x1 = *(const float4*)((const float*)a.q + qrow + d0 + 4);
+                        f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
+                        f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+                    }
+                    const float* ks = a.k_scale + (int64_t)(seg % n_kv) * HD + d0;
+                    const float4 k0 = *(const float4*)ks;
+                    const float4 k1 = *(const float4*)(ks + 4);
+                    f[0] *= k0.x; f[1] *= k0.y; f[2] *= k0.z; f[3] *= k0.w;
+                    f[4] *= k1.x; f[5] *= k1.y; f[6] *= k1.z; f[7] *= k1.w;
+                }
+                uint32_t h16[8], l16[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    split_bf16(f[e], h16[e], l16[e]);
+                    part += __uint_as_float(h16[e] << 16) + __uint_as_float(l16[e] << 16);
+                }
+                u32x4 hv = {h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16),
+                            h16[4] | (h16[5] << 16), h16[6] | (h16[7] << 16)};
+                u32x4 lv = {l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16),
+                            l16[4] | (l16[5] << 16), l16[6] | (l16[7] << 16)};
+                qhi[c] = __builtin_bit_cast(bf16x8, hv);
+                qlo[c] = __builtin_bit_cast(bf16x8, lv);
+            } else if (QT == DT_BF16) {
                 uint4 w = make_uint4(0, 0, 0, 0);
                 if (live) w = ld16((const char*)a.q + (qrow + d0) * 2);
                 qhi[c] = __builtin_bit_cast(bf16x8, w);
@@ -367,6 +414,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 qlo[c] = __builtin_bit_cast(bf16x8, lv);
             }
         }
+        if constexpr (I4) cq = kInt4Bias * sum_rows4(part);
     };
 
     // ---- per-piece online-softmax state
@@ -375,6 +423,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     f32x4 acc[T::NT];
 #pragma unroll
     for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+    float w_run = 0.0f;   // 4-bit: sum of the value weights (hi + lo) fed to the PV product
     bool piece_bad = false;
     bool piece_whole = false;   // the current piece began at its segment's first block
     int q_seg = -1;
@@ -436,6 +485,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     auto vsc_of = [&](int i) { return QUANT ? meta_f(A.vsc, Bm.vsc, i) : 1.0f; };
 
     uint4 kr[kDepth][T::LOADS], vr[kDepth][T::LOADS];
+    f32x4 vsr[kDepth];   // 4-bit: value scales of this lane's 4 tokens
     uint2 nkr[kDepth], nvr[kDepth];   // fused step: 8 B of the new K / V row per lane
     char* newk = newrow_all + wave * 1024;
     char* newv = newk + 512;
@@ -456,6 +506,24 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         // bf16 K: contiguous 1 KiB per load instruction (staged through LDS
         // into the operand layout); 8-bit K: straight into the operand
         // registers, lane (t, grp) taking 16 B of token row t
+        if constexpr (I4) {
+            // 4-bit tile: lane (t, grp) takes the LB bytes of token row t
+            // holding channels (d_h / 4) grp .. +d_h / 4, for K (straight
+            // into the operand) and V (through LDS) alike, and the value
+            // scales of its tokens 4 grp .. 4 grp + 3
+            const int off = col * T::ROWB + grp * T::LB;
+            if constexpr (T::LB == 16) {
+                kr[s][0] = ld16_stream(kt + off);
+                vr[s][0] = ld16_stream(vt + off);
+            } else {
+                const u32x2 kk = __builtin_nontemporal_load((const u32x2*)(kt + off));
+                const u32x2 vv = __builtin_nontemporal_load((const u32x2*)(vt + off));
+                kr[s][0] = make_uint4(kk.x, kk.y, 0, 0);
+                vr[s][0] = make_uint4(vv.x, vv.y, 0, 0);
+            }
+            vsr[s] = *(const f32x4*)(a.v_scale + ((int64_t)pb * n_kv + j) * 16 + 4 * grp);
+            return;
+        }
         const int koff = KST ? 16 * lane : col * T::ROWB + 16 * grp;
         const int kstep = KST ? 1024 : 64;
         if (a.k_new != nullptr && ((info >> 6) & 1)) {
@@ -484,13 +552,16 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 
     auto flush = [&](int seg, bool whole) {
         float l_tot = sum_rows4(l_run);
+        // 4-bit: the V operand holds 136 + code, so the product carries
+        // 136 * (sum of the weights it was fed); remove it
+        const float off = I4 ? kInt4Bias * sum_rows4(w_run) : 0.0f;
         if (piece_bad) l_tot = __builtin_nanf("");
         if (col < g) {
             const int64_t prow = whole ? (int64_t)seg * g + col : ((int64_t)seg + wg) * g + col;
             f32x4 r[T::NT];
             const float inv = l_tot != 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
-            for (int t = 0; t < T::NT; ++t) r[t] = acc[t] * inv;
+            for (int t = 0; t < T::NT; ++t) r[t] = (I4 ? acc[t] - off : acc[t]) * inv;
             if (!whole) {
 #pragma unroll
                 for (int t = 0; t < T::NT; ++t)
@@ -512,6 +583,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         }
         m_run = -__builtin_inff();
         l_run = 0.0f;
+        w_run = 0.0f;
 #pragma unroll
         for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
         piece_bad = false;
@@ -544,13 +616,15 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 a.seg_info[seg] = make_int2(wg, last_wave);
             }
         }
+        // 4-bit value scales of this block, taken before the slot is refilled
+        const f32x4 vsb = I4 ? vsr[s] : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
         const int pb_i = meta_id(i);
         // block scales, read while every lane is active (a readlane inside a
         // divergent branch would read an unselected lane's stale register)
         const float ksc = ksc_of(i);
         const float vsc = vsc_of(i);
         if (pb_i < 0) piece_bad = true;
-        if (a.k_new != nullptr && seg_last && pb_i >= 0) {
+        if (!I4 && a.k_new != nullptr && seg_last && pb_i >= 0) {
             // fused decode step: this block holds the row's newest position
             // n - 1; its K/V rows come from the new token (replacing what
             // the tile load brought) and are written to the cache slot
@@ -608,7 +682,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 }
             }
         }
-        if (mask != 0xFFFFu) {
+        if (!I4 && mask != 0xFFFFu) {
             // rows past the sequence's end (or outside the window) may hold
             // stale data, possibly NaN: zero them so 0-weight products stay 0
 #pragma unroll
@@ -616,8 +690,16 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 if (!((mask >> vrow[l]) & 1u)) vr[s][l] = make_uint4(0, 0, 0, 0);
         }
         // stage V (as bf16) into this wave's LDS tile
+        if constexpr (I4) {
+            // lane (t, grp): token row t, channels (d_h / 4) grp .. in groups of 8
+            const uint32_t vw[4] = {vr[s][0].x, vr[s][0].y, vr[s][0].z, vr[s][0].w};
 #pragma unroll
-        for (int l = 0; l < T::LOADS; ++l) {
+            for (int c = 0; c < T::LB / 4; ++c)
+                *(bf16x8*)(stage + lds_off<HD>(col, (HD / 32) * grp + c)) =
+                    int4x8_to_bf16_biased(vw[c]);
+        }
+#pragma unroll
+        for (int l = 0; l < (I4 ? 0 : T::LOADS); ++l) {
             if (KV == DT_BF16) {
                 *(uint4*)(stage + lds_off<HD>(vrow[l], vcb[l])) = vr[s][l];
             } else {
@@ -642,11 +724,17 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 #pragma unroll
         for (int c = 0; c < T::NCH; ++c) {
             bf16x8 kop;
-            if constexpr (KST)
+            if constexpr (KST) {
                 kop = *(const bf16x8*)(kstage + col * T::ROWB + 16 * ((4 * c + grp) ^ kswz<HD>(col)));
-            else kop = kv_operand_from_bytes<KV>(kr[s][c / 2], c % 2);
+            } else if constexpr (I4) {
+                const uint32_t kw[4] = {kr[s][0].x, kr[s][0].y, kr[s][0].z, kr[s][0].w};
+                kop = int4x8_to_bf16_biased(kw[c]);
+            } else {
+                kop = kv_operand_from_bytes<KV>(kr[s][c / 2], c % 2);
+            }
             st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[c], st, 0, 0, 0);
-            if (QT == DT_F32) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
+            if (QT == DT_F32 || I4)
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
         }
         // refill this slot with the block kDepth ahead
         if (refill) issue(s, i + kDepth);
@@ -656,7 +744,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         float sv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sv[e] = st[e] * mult;
+            sv[e] = (I4 ? st[e] - cq : st[e]) * mult;
             if (!((mask >> (4 * grp + e)) & 1u)) sv[e] = -__builtin_inff();
         }
         const float mx = max_rows4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
@@ -671,6 +759,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             const float alpha = m_run == -__builtin_inff() ? 0.0f
                                                            : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
+            w_run *= alpha;
 #pragma unroll
             for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
             m_run = m_new;
@@ -691,7 +780,10 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         // then a permlane16 swap regroups them.
         uint32_t hi16[4], lo16[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split_bf16(pe[e] * vsc, hi16[e], lo16[e]);
+        for (int e = 0; e < 4; ++e) {
+            split_bf16(pe[e] * (I4 ? vsb[e] : vsc), hi16[e], lo16[e]);
+            if (I4) w_run += __uint_as_float(hi16[e] << 16) + __uint_as_float(lo16[e] << 16);
+        }
         uint32_t H[2] = {hi16[0] | (hi16[1] << 16), hi16[2] | (hi16[3] << 16)};
         uint32_t L[2] = {lo16[0] | (lo16[1] << 16), lo16[2] | (lo16[3] << 16)};
 #pragma unroll
@@ -764,7 +856,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
 #define PDA_BY_KV(HD)                                         \
     if (a.kv_dtype == DT_BF16) { PDA_BY_Q(HD, DT_BF16); }     \
     else if (a.kv_dtype == DT_FP8) { PDA_BY_Q(HD, DT_FP8); }  \
-    else { PDA_BY_Q(HD, DT_INT8); }
+    else if (a.kv_dtype == DT_INT8) { PDA_BY_Q(HD, DT_INT8); } \
+    else { PDA_BY_Q(HD, DT_INT4); }
     if (a.d_h == 128) { PDA_BY_KV(128); }
     else { PDA_BY_KV(64); }
 #undef PDA_BY_KV

@@ -14,7 +14,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // dtype codes, equal to pda_dtype
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT8 = 3 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT8 = 3, DT_INT4 = 4 };
 
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -201,6 +201,28 @@ __device__ __forceinline__ int row_prefix_len(int n, int pl, int max_blocks, int
     if (n == 0) return 0;
     if (pl < 0 || pl > prefix_blocks || pl >= ((n + 15) >> 4)) return -1;
     return pl;
+}
+
+// One packed group of 8 four-bit channels (a dword: byte i holds channel i
+// in its low nibble and channel i + 4 in its high nibble, each stored as
+// code + 8) -> the bf16 values 128 + nibble = 136 + code, in channel order.
+// 128 + n is exact in bf16 (exponent 2^7, mantissa unit 1), so the bytes are
+// only moved: v_perm_b32 pairs each nibble with the exponent byte 0x43.
+__device__ __forceinline__ bf16x8 int4x8_to_bf16_biased(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;          // channels 0..3
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // channels 4..7
+    const uint32_t e = 0x43434343u;
+    const u32x4 r = {__builtin_amdgcn_perm(e, lo, 0x04010400u), __builtin_amdgcn_perm(e, lo, 0x04030402u),
+                     __builtin_amdgcn_perm(e, hi, 0x04010400u), __builtin_amdgcn_perm(e, hi, 0x04030402u)};
+    return __builtin_bit_cast(bf16x8, r);
+}
+constexpr float kInt4Bias = 136.0f;   // 128 + 8: the biased value minus the code
+
+// fp32 -> symmetric 4-bit code nibble: RNE(y) clamped to [-7, 7] (NaN -> 0),
+// returned as code + 8.
+__device__ __forceinline__ uint32_t quant_int4_nibble(float y) {
+    const float r = y != y ? 0.0f : fminf(fmaxf(__builtin_rintf(y), -7.0f), 7.0f);
+    return (uint32_t)((int)r + 8);
 }
 
 }  // namespace pda

@@ -154,7 +154,8 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
 // or none (zero / NaN rows, also written there) are skipped. With a shared
 // prefix (prefix_lens != nullptr), a row whose prefix has p blocks also has
 // the prefix pass's pieces of chunks 0 .. ceil(p / kPrefixChunk) - 1, at row
-// c * rows + r of pre_o / pre_ml, and its stream pieces always come here.
+// c * rows + r of pre_o / pre_ml, and its stream pieces always come here; a
+// 4-bit cache gives every row one extra piece there (its residual window).
 // With CS > 1 workgroups per row (grid.y), workgroup (row, cs) handles the
 // cs-th of CS column ranges, so rows with many pieces are spread over
 // several compute units. The weights live in dynamic LDS sized for the wave
@@ -177,6 +178,11 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
         const int pl = row_prefix_len(a.context_lens[b], a.prefix_lens[b], a.max_blocks,
                                       a.prefix_blocks);
         npre = pl > 0 ? (pl + kPrefixChunk - 1) / kPrefixChunk : 0;
+    } else if (a.extra_pieces > 0) {
+        // every valid row has its extra pieces (possibly empty); an invalid
+        // row keeps the NaN the attention kernel wrote
+        const int n = a.context_lens[row / a.n_q];
+        npre = (n >= 0 && n <= a.max_blocks * 16) ? a.extra_pieces : 0;
     }
     if (npre == 0 && np <= 1) return;
     const int64_t prow0 = (seg + info.x) * g + hh;
@@ -212,7 +218,8 @@ hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.n_q;
     if (rows == 0) return hipSuccess;
-    const int chunks = (a.prefix_blocks + kPrefixChunk - 1) / kPrefixChunk;
+    const int chunks = a.prefix_blocks > 0 ? (a.prefix_blocks + kPrefixChunk - 1) / kPrefixChunk
+                                           : a.extra_pieces;
     const size_t lds = (size_t)(a.nw + chunks) * sizeof(float);
     // split a row's columns over several workgroups only when segments
     // average many pieces (long sequences in a small batch)

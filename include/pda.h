@@ -62,7 +62,8 @@ typedef enum pda_dtype {
     PDA_F32 = 0,
     PDA_BF16 = 1,
     PDA_FP8_E4M3 = 2,
-    PDA_INT8 = 3
+    PDA_INT8 = 3,
+    PDA_INT4 = 4      /* 4-bit cache with a bf16 residual window (pda_*_int4 calls) */
 } pda_dtype;
 
 /* ------------------------------------------------------------------ misc */
@@ -344,6 +345,55 @@ int32_t pda_decode_step_prefix(const void* q, const void* k_new, const void* v_n
                                const int32_t* prefix_lens, float scale, void* out,
                                const pda_attn_desc* d, void* workspace, size_t ws_bytes,
                                void* stream);
+
+/* 4-bit KV cache with a full-precision residual window  [SoK paper section
+ * 2.3: keys quantized per channel and values per token, the most recent
+ * tokens held at full precision; section 4.3: 4-bit storage is near-free
+ * with per-channel keys; kv-cache tag page, KV-cache quantization teaser:
+ * entries are encoded when stored and reconstructed when attention reads
+ * them]. Storage (d = d_h, NB = num_blocks):
+ *   k_q, v_q   device uint8 [NB][n_kv][16][d/2]: 4-bit codes c in [-7, 7],
+ *              stored as the nibble c + 8; in each group of 8 channels
+ *              8k .. 8k+7, byte 4k + i holds channel 8k + i in its low nibble
+ *              and channel 8k + 4 + i in its high nibble
+ *   k_scale    device fp32 [n_kv][d]: key value = k_scale[j][ch] * c, one
+ *              fixed scale per (KV head, channel), chosen by the caller
+ *   v_scale    device fp32 [NB][n_kv][16]: value = v_scale[pb][j][t] * c, one
+ *              scale per token, set when its block is encoded
+ *   k_res, v_res device bf16 [B][n_kv][16][d]: each row's open block (its
+ *              newest n % 16 tokens) at full precision, token t at slot t % 16
+ * A row of n tokens keeps floor(n / 16) encoded blocks and n % 16 residual
+ * tokens. */
+
+/* Append of each row's newest token under that policy: for every row b with
+ * n = context_lens[b] > 0 (n counts the new token) and every KV head j, the
+ * residual slot (n - 1) % 16 of row b receives k_new[b][j][:] / v_new[b][j][:]
+ * (bit copy); when that fills the block ((n - 1) % 16 == 15) its 16 tokens
+ * are encoded into physical block block_table[b][(n - 1) / 16]:
+ *   keys:   c = RNE(x * fp32(1 / k_scale[j][ch])), clamped to [-7, 7]
+ *   values: s = fp32(amax_ch |x| / 7) (1 if the amax is 0 or not finite),
+ *           c = RNE(x * fp32(1 / s)), clamped; v_scale[pb][j][t] = s
+ * k_new, v_new device bf16 [B][n_kv][d]. Descriptor: B, n_kv, d_h,
+ * block_size, max_blocks_per_seq, num_blocks, kv_dtype = PDA_INT4; rows with
+ * n <= 0 or n > max_blocks_per_seq * 16, or an unmapped block to encode,
+ * append nothing. Errors: EINVAL, EHIP. */
+int32_t pda_kv_append_int4(const void* k_new, const void* v_new, const int32_t* block_table,
+                           const int32_t* context_lens, void* k_q, void* v_q,
+                           const float* k_scale, float* v_scale, void* k_res, void* v_res,
+                           const pda_attn_desc* d, void* stream);
+
+/* Paged decode attention over that cache: as pda_paged_decode_attn, with
+ * row b's positions t < 16 * floor(n / 16) read from its encoded blocks
+ * (decoded as above) and the rest from its residual buffer. kv_dtype =
+ * PDA_INT4, q bf16 or fp32, window 0. The workspace is required
+ * (pda_attn_workspace_size of the same descriptor). Row semantics and
+ * errors as for pda_paged_decode_attn. */
+int32_t pda_paged_decode_attn_int4(const void* q, const void* k_q, const void* v_q,
+                                   const float* k_scale, const float* v_scale,
+                                   const void* k_res, const void* v_res,
+                                   const int32_t* block_table, const int32_t* context_lens,
+                                   float scale, void* out, const pda_attn_desc* d,
+                                   void* workspace, size_t ws_bytes, void* stream);
 
 /* Log-sum-exp merge of split-KV partial results. For each of `rows` rows and
  * P partials with (o_p, m_p, l_p):
