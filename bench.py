@@ -111,6 +111,19 @@ def oracle_leg(w, inp, table, slots, shared, host):
     otable, oslots = opool.build_block_table(inp.ctx, w.block_size, table.shape[1], osh)
     tables_equal = bool((otable == table).all() and (oslots == slots).all()
                         and list(osh) == [int(x) for x in shared])
+    if w.kv_dtype == 4:
+        # 4-bit cache: the oracle's residual-window append, then attention
+        from oracle import int4
+        st = int4.kv_append_int4({"k": host["k"], "v": host["v"], "v_scale": host["vs"],
+                                  "k_res": host["k_res"], "v_res": host["v_res"]},
+                                 host["kn_raw"], host["vn_raw"], otable, inp.ctx, host["ks"])
+        t0 = time.perf_counter()
+        out, _, _, bad = oracle.paged_attn_int4(host["q"], st, host["ks"], otable, inp.ctx,
+                                                w.softmax_scale, n_q=w.n_q, n_kv=w.n_kv,
+                                                q_dtype=w.q_dtype)
+        secs = time.perf_counter() - t0
+        return {"secs": secs, "threads": oracle.num_threads(), "bad_rows": bad,
+                "tables_equal": tables_equal}, out
     k = oracle.kv_append(host["k"], host["kn_raw"], oslots) if w.kv_dtype in (0, 1) else \
         oracle.kv_append_quant(host["k"], host["ks"], host["kn_f32"], oslots, w.kv_dtype)
     v = oracle.kv_append(host["v"], host["vn_raw"], oslots) if w.kv_dtype in (0, 1) else \
@@ -140,10 +153,12 @@ def host_snapshot(w, inp):
     h = {"q": raw(inp.q), "k": raw(inp.k_cache), "v": raw(inp.v_cache)}
     kn, vn = raw(inp.k_new), raw(inp.v_new)
     h["kn_raw"], h["vn_raw"] = kn, vn
-    if w.kv_dtype in (2, 3):
+    if w.kv_dtype in (2, 3, 4):
         h["ks"], h["vs"] = inp.k_scale.cpu().numpy(), inp.v_scale.cpu().numpy()
         h["kn_f32"] = synth.bf16_bits_to_f32(kn)
         h["vn_f32"] = synth.bf16_bits_to_f32(vn)
+    if w.kv_dtype == 4:
+        h["k_res"], h["v_res"] = raw(inp.k_res), raw(inp.v_res)
     return h
 
 
@@ -228,6 +243,8 @@ def main(argv=None) -> int:
         return 2
     w = synth.WORKLOADS[args.workload]
     quant = w.kv_dtype in (synth.FP8, synth.INT8)
+    int4 = w.kv_dtype == synth.INT4
+    fused = args.fused and not int4   # the 4-bit cache appends and attends in two calls
 
     _say(f"[bench] workload {w.name}: drawing inputs")
     inp, pool, shared, table, slots = build_inputs(w, dev)
@@ -256,7 +273,16 @@ def main(argv=None) -> int:
     ws = pda.workspace_for(desc, dev)
     scale = w.softmax_scale
 
-    if cascade:
+    if int4:
+        def append():
+            pda.kv_append_int4(inp.k_new, inp.v_new, bt, cl, inp.k_cache, inp.v_cache,
+                               inp.k_scale, inp.v_scale, inp.k_res, inp.v_res, desc=desc)
+
+        def attend():
+            pda.paged_decode_attn_int4(inp.q, inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale,
+                                       inp.k_res, inp.v_res, bt, cl, scale, out, desc=desc,
+                                       workspace=ws)
+    elif cascade:
         def append():
             if quant:
                 pda.kv_append_quant(inp.k_new, inp.v_new, sl, inp.k_cache, inp.v_cache,
@@ -285,7 +311,9 @@ def main(argv=None) -> int:
             pda.paged_decode_attn(inp.q, inp.k_cache, inp.v_cache, bt, cl, scale, out,
                                   desc=desc, workspace=ws)
 
-    if args.fused:
+    if int4:
+        desc.new_dtype = synth.BF16
+    if fused:
         desc.new_dtype = synth.BF16 if w.kv_dtype != synth.F32 else synth.F32
 
         def step():
@@ -413,7 +441,7 @@ def main(argv=None) -> int:
         got = out.cpu().numpy().reshape(w.B * w.n_q, w.d_h).astype(np.float64)
         _say("[bench] oracle leg (fp64, host cores)")
         info, ref = oracle_leg(w, inp, table, slots, shared, host)
-        tol = 3e-2 if quant else 5e-3
+        tol = 3e-2 if (quant or int4) else 5e-3
         err = float(np.abs(got - ref).max()) if np.isfinite(got).all() else float("inf")
         parity = {"rows": int(ref.shape[0]), "max_abs_err": err, "tol": tol,
                   "pass": bool(err < tol and info["bad_rows"] == 0 and info["tables_equal"]),
@@ -467,7 +495,7 @@ def main(argv=None) -> int:
         "cold_GBps_median": (None if not cold_ms else
                              round(att_bytes / (_pct(cold_ms, 50) * 1e-3) / 1e9, 1)),
         "logical_GBps": round(sb.attention / (att_avg * 1e-3) / 1e9, 1),
-        "timing": ("fused decode step; " if args.fused else "") +
+        "timing": ("fused decode step; " if fused else "append + attention calls; ") +
                   ("graph replay of the step" if graph is not None else "eager launches") +
                   "; per-call averages from back-to-back calls between two HIP events" +
                   (f"; cold: {len(cold_ms)} single calls, each after a 1 GiB cache-evicting "

@@ -118,9 +118,12 @@ def step_bytes(context_lens: Sequence[int], *, n_q: int, n_kv: int, d_h: int, bl
                window: int = 0, sinks: int = 0) -> StepBytes:
     """Bytes one decode step must move (SoK appendix A.1 accounting); with a
     sliding window only the attended positions count."""
-    w_kv = ELEM_BYTES[kv_dtype]
     w_q = ELEM_BYTES[q_dtype]
     B = len(context_lens)
+    if kv_dtype == 4:
+        return _step_bytes_int4(context_lens, n_q=n_q, n_kv=n_kv, d_h=d_h, w_q=w_q,
+                                out_bytes=out_bytes, appended_tokens=appended_tokens)
+    w_kv = ELEM_BYTES[kv_dtype]
     tokens = sum(attended_tokens(int(n), window, sinks) for n in context_lens)
     blocks = [attended_blocks(int(n), block_size, window, sinks) for n in context_lens]
     kv = 2 * tokens * n_kv * d_h * w_kv
@@ -141,6 +144,26 @@ def step_bytes(context_lens: Sequence[int], *, n_q: int, n_kv: int, d_h: int, bl
         out_write=B * n_q * d_h * out_bytes,
         append_read=2 * T * n_kv * d_h * w_new + 8 * T,
         append_write=2 * T * n_kv * d_h * w_kv)
+
+
+def _step_bytes_int4(context_lens, *, n_q, n_kv, d_h, w_q, out_bytes, appended_tokens):
+    """4-bit cache with a residual window: each row's floor(n / 16) encoded
+    blocks (half a byte per K and V element, a 4-B value scale per token and
+    KV head) plus its n % 16 residual tokens in bf16; the per-channel key
+    scales once; the block-table entries of the encoded blocks. The append
+    writes the new rows into the residual buffers."""
+    B = len(context_lens)
+    full = sum((int(n) // 16) * 16 for n in context_lens)
+    res = sum(int(n) % 16 for n in context_lens)
+    kv = n_kv * d_h * (full + 4 * res)            # 2 (K, V) * (0.5 * full + 2 * res)
+    T = B if appended_tokens is None else appended_tokens
+    return StepBytes(
+        kv_read=kv, kv_read_unique=kv, q_read=B * n_q * d_h * w_q,
+        table_read=4 * (full // 16), lens_read=4 * B,
+        scales_read=4 * n_kv * full + 4 * n_kv * d_h,
+        out_write=B * n_q * d_h * out_bytes,
+        append_read=2 * T * n_kv * d_h * 2 + 4 * T,
+        append_write=2 * T * n_kv * d_h * 2)
 
 
 def step_flops(context_lens: Sequence[int], n_q: int, d_h: int) -> int:

@@ -186,8 +186,8 @@ def attn_desc(q, k_cache, block_table, *, max_context: int, out_dtype: int = F32
               prefix_blocks: int = 0) -> AttnDesc:
     B, n_q, d_h = q.shape
     nb, n_kv, bs, d2 = k_cache.shape
-    assert d2 == d_h
     kvd = kv_dtype if kv_dtype is not None else dtype_code(k_cache)
+    assert d2 == d_h or (kvd == INT4 and 2 * d2 == d_h)   # 4-bit: two codes per byte
     return AttnDesc(B, n_q, n_kv, d_h, bs, int(block_table.shape[1]), nb, kvd, dtype_code(q),
                     out_dtype, int(max_context), int(num_partitions), int(total_context),
                     int(reuse_prefix_blocks), int(window), int(sink_tokens),

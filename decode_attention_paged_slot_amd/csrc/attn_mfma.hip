@@ -55,7 +55,13 @@ namespace {
 #ifndef PDA_ATTN_DEPTH
 #define PDA_ATTN_DEPTH 2
 #endif
+#ifndef PDA_INT4_DEPTH
+#define PDA_INT4_DEPTH 4
+#endif
 constexpr int kDepth = PDA_ATTN_DEPTH;   // blocks in flight per wave beyond the one being consumed
+// 4-bit tiles are a quarter of a bf16 tile: more of them in flight per wave
+// keep as many bytes outstanding
+constexpr int kDepthInt4 = PDA_INT4_DEPTH;
 constexpr float kSlack = 8.0f;   // lazy-rescaling threshold (weights < 2^8)
 
 template <int HD, int KV>
@@ -143,6 +149,7 @@ struct Meta {
 
 template <int HD, int KV, int QT>
 __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mfma(AttnArgs a) {
+    constexpr int kDepth = KV == DT_INT4 ? kDepthInt4 : pda::kDepth;   // this kernel's depth
     using T = Tr<HD, KV>;
     constexpr bool QUANT = KV == DT_FP8 || KV == DT_INT8;   // 8-bit, per-(block, head) scales
     constexpr bool I4 = KV == DT_INT4;   // 4-bit: per-channel K and per-token V scales

@@ -32,9 +32,9 @@ import numpy as np
 
 # dtype tags used across the repository's Python code (kept in sync with the
 # C headers by value, not by import: 0 f32, 1 bf16, 2 fp8 e4m3 (OCP), 3 int8)
-F32, BF16, FP8, INT8 = 0, 1, 2, 3
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", INT8: "int8"}
-ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1, INT8: 1}
+F32, BF16, FP8, INT8, INT4 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", INT8: "int8", INT4: "int4"}
+ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1, INT8: 1, INT4: 0.5}
 BF16_NAN = np.uint16(0x7FC0)
 FP8_NAN = np.uint8(0x7F)
 
@@ -95,8 +95,14 @@ QUANT_PREFIX_INT8 = QUANT_PREFIX_FP8.with_(name="quant_prefix_int8", seed=6, kv_
 LLAMA70B_WINDOW = LLAMA70B_LAYER.with_(name="llama3_70b_layer_b8_32k_window4k_sinks4", seed=7,
                                        attn_window=4096, attn_sinks=4)
 
+# The 70B layer on a 4-bit cache with a residual window: contexts end at
+# every residual length, so some rows fill a block in this step.
+LLAMA70B_INT4 = LLAMA70B_LAYER.with_(name="llama3_70b_layer_b8_32k_int4", seed=8, kv_dtype=INT4,
+                                     ctx_lo=32753, ctx_hi=32768)
+
 WORKLOADS = {w.name: w for w in (TINY_MHA, LLAMA8B_LAYER, LLAMA70B_LAYER, LONG_SINKS,
-                                 QUANT_PREFIX_FP8, QUANT_PREFIX_INT8, LLAMA70B_WINDOW)}
+                                 QUANT_PREFIX_FP8, QUANT_PREFIX_INT8, LLAMA70B_WINDOW,
+                                 LLAMA70B_INT4)}
 
 
 # ---------------------------------------------------------------- primitives
@@ -191,6 +197,8 @@ def make_host_inputs(w: Workload, seed: Optional[int] = None, with_new: bool = T
     owned by a sequence is decided by the block-table builder from
     `free_order`, after which `poison_unowned` marks the rest as NaN.
     """
+    if w.kv_dtype == INT4:
+        raise ValueError("4-bit cache inputs are drawn on the device (make_device_inputs)")
     r = rng(w.seed if seed is None else seed)
     ctx = context_lengths(w, r)
     nb = pool_size(w, ctx)
@@ -309,6 +317,18 @@ class DeviceInputs:
     v_scale: "object" = None
     k_new: "object" = None
     v_new: "object" = None
+    k_res: "object" = None     # 4-bit cache: residual buffers [B][n_kv][16][d_h] bf16
+    v_res: "object" = None
+
+
+def _device_int4(shape, gen, device):
+    """4-bit cache bytes drawn as codes: two independent codes per byte, each
+    round(2 N(0,1)) clamped to [-7, 7] and stored as code + 8."""
+    import torch
+    def nib():
+        c = torch.randn(shape, generator=gen, device=device).mul_(2.0).round_().clamp_(-7, 7)
+        return (c + 8).to(torch.uint8)
+    return nib() | (nib() << 4)
 
 
 def _device_quantized(shape, dtype: int, gen, device):
@@ -343,8 +363,20 @@ def make_device_inputs(w: Workload, device, seed: Optional[int] = None,
     qdt = torch.bfloat16 if w.q_dtype == BF16 else torch.float32
     q = torch.randn((w.B, w.n_q, w.d_h), generator=gen, device=device).to(qdt)
     shape = (nb, w.n_kv, w.block_size, w.d_h)
-    ks = vs = None
-    if w.kv_dtype in (F32, BF16):
+    ks = vs = kres = vres = None
+    if w.kv_dtype == INT4:
+        # codes, per-channel key scales (every 32nd channel an 8x outlier),
+        # per-token value scales, bf16 residual windows
+        cshape = (nb, w.n_kv, w.block_size, w.d_h // 2)
+        k = _device_int4(cshape, gen, device)
+        v = _device_int4(cshape, gen, device)
+        mag = torch.where(torch.arange(w.d_h, device=device) % 32 == 5, 8.0, 1.0)
+        ks = (0.15 + 0.15 * torch.rand((w.n_kv, w.d_h), generator=gen, device=device)) * mag
+        vs = 0.1 + 0.4 * torch.rand((nb, w.n_kv, w.block_size), generator=gen, device=device)
+        rshape = (w.B, w.n_kv, w.block_size, w.d_h)
+        kres = torch.randn(rshape, generator=gen, device=device).to(torch.bfloat16)
+        vres = torch.randn(rshape, generator=gen, device=device).to(torch.bfloat16)
+    elif w.kv_dtype in (F32, BF16):
         kdt = torch.bfloat16 if w.kv_dtype == BF16 else torch.float32
         k = torch.randn(shape, generator=gen, device=device).to(kdt)
         v = torch.randn(shape, generator=gen, device=device).to(kdt)
@@ -357,7 +389,7 @@ def make_device_inputs(w: Workload, device, seed: Optional[int] = None,
         kn = torch.randn((w.B, w.n_kv, w.d_h), generator=gen, device=device).to(ndt)
         vn = torch.randn((w.B, w.n_kv, w.d_h), generator=gen, device=device).to(ndt)
     sp = w.shared_prefix_tokens // w.block_size if w.shared_prefix_tokens else 0
-    return DeviceInputs(w, ctx, nb, order, sp, q, k, v, ks, vs, kn, vn)
+    return DeviceInputs(w, ctx, nb, order, sp, q, k, v, ks, vs, kn, vn, kres, vres)
 
 
 def poison_unowned_device(w: Workload, inp: DeviceInputs, block_table: np.ndarray) -> None:
@@ -370,6 +402,22 @@ def poison_unowned_device(w: Workload, inp: DeviceInputs, block_table: np.ndarra
     for b in range(block_table.shape[0]):
         nblk = (int(inp.ctx[b]) + bs - 1) // bs
         owned[block_table[b, :nblk]] = True
+    if w.kv_dtype == INT4:
+        # blocks not yet encoded (free, or behind a residual window) get NaN
+        # value scales; residual slots past the newest token get NaN rows
+        # (the slots a filling append encodes from stay intact)
+        full = np.zeros(inp.num_blocks, dtype=bool)
+        for b in range(block_table.shape[0]):
+            full[block_table[b, :int(inp.ctx[b]) // bs]] = True
+        idx = torch.from_numpy(np.nonzero(~full)[0]).to(dev)
+        if idx.numel():
+            inp.v_scale[idx] = float("nan")
+        for b in range(block_table.shape[0]):
+            n = int(inp.ctx[b])
+            first = (n - 1) % bs + 1 if n > 0 else 0
+            inp.k_res[b, :, first:, :] = float("nan")
+            inp.v_res[b, :, first:, :] = float("nan")
+        return
     free = torch.from_numpy(np.nonzero(~owned)[0]).to(dev)
     if w.kv_dtype == F32:
         nan = float("nan")

@@ -27,7 +27,8 @@ FULL = ["tiny_mha", "llama3_8b_layer", "llama3_70b_layer_b8_32k", "long_context_
         "quant_prefix_fp8", "quant_prefix_int8", "llama3_70b_layer_b8_32k_window4k_sinks4",
         # the shared-prefix workloads again through the fused shared-prefix step
         # (each shared block read once), the benchmark's launch for them
-        "quant_prefix_fp8:prefix", "quant_prefix_int8:prefix"]
+        "quant_prefix_fp8:prefix", "quant_prefix_int8:prefix",
+        "llama3_70b_layer_b8_32k_int4"]
 
 
 def _raw(t):
@@ -75,6 +76,9 @@ def test_full_size_workload(name):
     synth.apply_sinks_device(w, inp, table)
     synth.poison_unowned_device(w, inp, table)
     torch.cuda.synchronize()
+    if w.kv_dtype == synth.INT4:
+        _full_size_int4(w, inp, table)
+        return
     q_h, k_h, v_h = _raw(inp.q), _raw(inp.k_cache), _raw(inp.v_cache)
     kn_h, vn_h = _raw(inp.k_new), _raw(inp.v_new)
     quant = w.kv_dtype in (synth.FP8, synth.INT8)
@@ -146,3 +150,47 @@ def test_full_size_workload(name):
     print(f"  {name}: rows={rows.size} max-abs={err:.3g} (tol {tol}) "
           f"plan={pda.attn_plan(desc)}", flush=True)
     assert err < tol
+
+
+def _full_size_int4(w, inp, table):
+    """4-bit cache: the residual-window append (state bit for bit against the
+    oracle's append), then attention on sampled rows against the oracle."""
+    import torch
+    import decode_attention_paged_slot_amd as pda
+    from oracle import int4
+    dev = inp.q.device
+    st = {"k": _raw(inp.k_cache), "v": _raw(inp.v_cache), "v_scale": inp.v_scale.cpu().numpy(),
+          "k_res": _raw(inp.k_res), "v_res": _raw(inp.v_res)}
+    ks = inp.k_scale.cpu().numpy()
+    q_h, kn_h, vn_h = _raw(inp.q), _raw(inp.k_new), _raw(inp.v_new)
+    bt = torch.from_numpy(table).to(dev)
+    cl = torch.from_numpy(inp.ctx).to(dev)
+    desc = pda.attn_desc(inp.q, inp.k_cache, bt, max_context=int(inp.ctx.max()),
+                         kv_dtype=synth.INT4, total_context=int(inp.ctx.sum()),
+                         new_dtype=synth.BF16)
+    pda.kv_append_int4(inp.k_new, inp.v_new, bt, cl, inp.k_cache, inp.v_cache, inp.k_scale,
+                       inp.v_scale, inp.k_res, inp.v_res, desc=desc)
+    out = torch.full((w.B, w.n_q, w.d_h), float("nan"), device=dev)
+    pda.paged_decode_attn_int4(inp.q, inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale,
+                               inp.k_res, inp.v_res, bt, cl, w.softmax_scale, out, desc=desc,
+                               workspace=pda.workspace_for(desc, dev))
+    torch.cuda.synchronize()
+    st2 = int4.kv_append_int4(st, kn_h, vn_h, table, inp.ctx, ks)
+    assert (_raw(inp.k_res) == st2["k_res"]).all() and (_raw(inp.v_res) == st2["v_res"]).all()
+    filled = [int(table[b, (int(n) - 1) // 16]) for b, n in enumerate(inp.ctx) if n % 16 == 0]
+    print(f"  int4: {len(filled)} rows filled a block this step", flush=True)
+    got_vs = inp.v_scale.cpu().numpy()
+    for pb in filled:
+        assert (_raw(inp.k_cache[pb]) == st2["k"][pb]).all()
+        assert (_raw(inp.v_cache[pb]) == st2["v"][pb]).all()
+        assert (got_vs[pb].view(np.uint32) == st2["v_scale"][pb].view(np.uint32)).all()
+    rows = _sample_rows(w, np.random.default_rng(w.seed + 100))
+    ref, _, _, bad = oracle.paged_attn_int4(q_h, st2, ks, table, inp.ctx, w.softmax_scale,
+                                            n_q=w.n_q, n_kv=w.n_kv, q_dtype=w.q_dtype, rows=rows)
+    assert bad == 0
+    got = out.reshape(w.B * w.n_q, w.d_h)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    assert np.isfinite(got).all()
+    err = float(np.abs(got.astype(np.float64) - ref).max())
+    print(f"  {w.name}: rows={rows.size} max-abs={err:.3g} (tol {TOL_8BIT}) "
+          f"plan={pda.attn_plan(desc)}", flush=True)
+    assert err < TOL_8BIT
