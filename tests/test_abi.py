@@ -194,3 +194,30 @@ def test_prefix_calls_check_the_descriptor_first():
     rc = binding._lib.pda_paged_decode_attn_prefix(*null13, 1.0, None,
                                                    binding.ctypes.byref(d4), None, 0, None)
     assert rc == binding.EINVAL and "NULL" in pda.last_error()
+
+
+def test_int4_descriptor_rules():
+    d = _desc(kv_dtype=pda.INT4, num_partitions=1)
+    # a 4-bit cache always goes through the merge (its residual-window piece):
+    # split bookkeeping plus one extra piece per output row
+    assert pda.attn_workspace_size(d) == _ws_parts(d) + \
+        (d.B * d.n_q * d.d_h * 4 + 255) // 256 * 256 + (d.B * d.n_q * 2 * 4 + 255) // 256 * 256
+    null = (None,) * 9
+    # only the int4 calls take it, and no window or shared prefix with it
+    rc = binding._lib.pda_paged_decode_attn(None, None, None, None, None, 1.0, None,
+                                            binding.ctypes.byref(d), None, 0, None)
+    assert rc == binding.EINVAL
+    rc = binding._lib.pda_paged_decode_attn_quant(*(None,) * 7, 1.0, None,
+                                                  binding.ctypes.byref(d), None, 0, None)
+    assert rc == binding.EINVAL
+    for bad in (dict(window=16), dict(prefix_blocks=1)):
+        rc = binding._lib.pda_paged_decode_attn_int4(*null, 1.0, None,
+                                                     binding.ctypes.byref(_desc(kv_dtype=pda.INT4,
+                                                                                **bad)),
+                                                     None, 0, None)
+        assert rc == binding.EINVAL
+    rc = binding._lib.pda_paged_decode_attn_int4(*null, 1.0, None, binding.ctypes.byref(
+        _desc(kv_dtype=pda.BF16)), None, 0, None)
+    assert rc == binding.EINVAL
+    rc = binding._lib.pda_kv_append_int4(*(None,) * 10, binding.ctypes.byref(d), None)
+    assert rc == binding.EINVAL and "NULL" in pda.last_error()

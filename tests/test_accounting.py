@@ -100,3 +100,18 @@ def test_window_accounting():
     # sinks and window sharing a block
     assert acc.attended_blocks(40, 16, 20, 5) == 3       # 0..4 -> block 0; 20..39 -> blocks 1, 2
     assert acc.attended_blocks(40, 16, 30, 5) == 3       # 0..4 and 10..39 share block 0
+
+
+def test_int4_accounting():
+    """4-bit cache with a residual window: half a byte per K and V element of
+    the encoded blocks (SoK paper section 2.3, w_q = w / 4 for bf16), a 4-B
+    value scale per encoded token and KV head, bf16 residual tokens, the
+    per-channel key scales once."""
+    sb = acc.step_bytes([20], n_q=4, n_kv=1, d_h=128, block_size=16, kv_dtype=4, q_dtype=1)
+    # 16 encoded tokens: 2 * 16 * 128 * 0.5 = 2048 B; 4 residual: 2 * 4 * 128 * 2 = 2048 B
+    assert sb.kv_read == 4096
+    assert sb.scales_read == 16 * 4 + 128 * 4
+    assert sb.table_read == 4                       # one encoded block
+    sb = acc.step_bytes([32, 15], n_q=8, n_kv=2, d_h=64, block_size=16, kv_dtype=4, q_dtype=1)
+    assert sb.kv_read == 2 * 2 * 64 * (32 // 2) + 2 * 2 * 64 * 15 * 2
+    assert sb.table_read == 8
