@@ -458,13 +458,19 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     // lanes address (lane L: token of panel row L / 4, columns
     // 16 t + 4 (L % 4) .. +3), so two reads (tokens base + 0..3, base + 4..7)
     // give the 8 tokens.
-    int trd0[T::NT], trd1[T::NT];
+    // The addresses include this wave's tile base and are formed once here;
+    // the empty asm makes each one opaque, so the compiler keeps it whole in
+    // a register rather than re-adding base and offset every block.
+    using lds_s16x4 = __attribute__((address_space(3))) s16x4;
+    uint32_t trd0[T::NT], trd1[T::NT];
+    const uint32_t stage_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)stage;
 #pragma unroll
     for (int t = 0; t < T::NT; ++t) {
         const int base = (grp & 1) * 8, q4 = lane & 3;
         const int r0 = base + ((lane & 15) >> 2);
-        trd0[t] = lds_off<HD>(r0, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
-        trd1[t] = lds_off<HD>(r0 + 4, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
+        trd0[t] = stage_lds + lds_off<HD>(r0, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
+        trd1[t] = stage_lds + lds_off<HD>(r0 + 4, 2 * t + (q4 >> 1)) + 8 * (q4 & 1);
+        asm volatile("" : "+v"(trd0[t]), "+v"(trd1[t]));
     }
 
     // metadata of the consumer's batch (A) and of the next one (Bm)
@@ -750,18 +756,24 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         const float mult = a.scale_log2 * ksc;
         float sv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = (I4 ? st[e] - cq : st[e]) * mult;
-            if (!((mask >> (4 * grp + e)) & 1u)) sv[e] = -__builtin_inff();
+        for (int e = 0; e < 4; ++e) sv[e] = (I4 ? st[e] - cq : st[e]) * mult;
+        if (mask != 0xFFFFu) {   // wave-uniform: a partial or windowed block
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!((mask >> (4 * grp + e)) & 1u)) sv[e] = -__builtin_inff();
         }
-        const float mx = max_rows4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+        const float lmx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         // Lazy rescaling: the reference max of a head moves only when the
         // block's max exceeds it by more than kSlack (log2 units), so the
         // weights stay below 2^kSlack and the accumulators are rescaled in
         // the rare blocks where some head's max jumps (the first block of a
         // piece always sets it). Any reference gives the same softmax: the
         // partial carries (reference, sum) together.
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+        if (__builtin_amdgcn_ballot_w64(lmx > m_run + kSlack) != 0) {
+            // some head's block max exceeds its reference by more than the
+            // slack (a head's max exceeds iff one of its four lanes' does):
+            // only then is the cross-lane max of each head formed
+            const float mx = max_rows4(lmx);
             const float m_new = mx > m_run + kSlack ? mx : m_run;
             const float alpha = m_run == -__builtin_inff() ? 0.0f
                                                            : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -806,10 +818,8 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         // O^T += [V^T | V^T] . [P_hi ; P_lo]
 #pragma unroll
         for (int t = 0; t < T::NT; ++t) {
-            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(stage + trd0[t]));
-            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(stage + trd1[t]));
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)trd0[t]);
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)trd1[t]);
             const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pop,
                                                               acc[t], 0, 0, 0);

@@ -72,7 +72,18 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
                                           void* out_row, int32_t out_dtype, float* wsh,
                                           float* red, f32x4* acc_sh) {
     constexpr int SUB = kThreads / V;  // partial subsets
+    constexpr int KP = 4;              // partial outputs loaded ahead per thread
     const int np = pr.n1 + pr.n2;
+    const int c = threadIdx.x % V, sub = threadIdx.x / V;
+    // The first KP partial outputs of this thread are loaded before the
+    // statistics are reduced, so the two phases share one memory round trip
+    // (a row has few pieces: most rows finish with these).
+    f32x4 ov[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int p = min(sub + k * SUB, np - 1);
+        ov[k] = np > 0 ? *((const f32x4*)pr.po(p) + c0 + c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     float mloc = -__builtin_inff();
     for (int p = threadIdx.x; p < np; p += kThreads) {
         const float2 x = *(const float2*)pr.ml(p);
@@ -87,10 +98,17 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
         lsum += w;
     }
     const float L = block_sum(lsum, red);   // its barriers also publish wsh
-    const int c = threadIdx.x % V, sub = threadIdx.x / V;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int p = sub + k * SUB;
+        if (p < np) {
+            const float w = wsh[p];
+            if (w != 0.0f) acc += w * ov[k];
+        }
+    }
 #pragma unroll 4
-    for (int p = sub; p < np; p += SUB) {
+    for (int p = sub + KP * SUB; p < np; p += SUB) {
         const f32x4 o = *((const f32x4*)pr.po(p) + c0 + c);
         const float w = wsh[p];
         if (w != 0.0f) acc += w * o;
