@@ -186,7 +186,7 @@ def stream_probe(dev, nbytes=2 << 30, reps=10):
 # Sources whose code decides what the attention call moves; a counter summary
 # under profiles/ is only used while they hash to the value it records.
 ATTN_SOURCES = ("attn_mfma.hip", "attn_prefix.hip", "attn_f32.hip", "merge.hip",
-                "device_common.h", "pda_internal.h", "api.cpp")
+                "append_int4.hip", "device_common.h", "pda_internal.h", "api.cpp")
 
 
 def attn_source_hash() -> str:

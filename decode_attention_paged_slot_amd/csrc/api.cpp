@@ -157,10 +157,9 @@ WsLayout ws_layout(const pda_attn_desc& d, const Plan& p) {
         w.part_ml_off = align256(slots * g * d.d_h * sizeof(float));
         w.seg_info_off = w.part_ml_off + align256(slots * g * 2 * sizeof(float));
         w.bytes = w.seg_info_off + align256(S * 2 * sizeof(int32_t));
-        if (d.prefix_blocks > 0 || d.kv_dtype == PDA_INT4) {
-            // prefix pass pieces, or the 4-bit cache's residual-window piece
-            const size_t chunks =
-                d.prefix_blocks > 0 ? (size_t)ceil_div(d.prefix_blocks, kPrefixChunk) : 1;
+        if (d.prefix_blocks > 0) {
+            // prefix pass pieces
+            const size_t chunks = (size_t)ceil_div(d.prefix_blocks, kPrefixChunk);
             const size_t rows = (size_t)d.B * d.n_q;
             w.pre_o_off = w.bytes;
             w.pre_ml_off = w.pre_o_off + align256(chunks * rows * d.d_h * sizeof(float));
@@ -392,8 +391,8 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     a.prefix_lens = prefix ? prefix_lens : nullptr;
     a.prefix_blocks = prefix ? d->prefix_blocks : 0;
     const bool int4 = kind == kInt4;
-    a.pre_o = prefix || int4 ? (float*)((char*)workspace + ws.pre_o_off) : nullptr;
-    a.pre_ml = prefix || int4 ? (float*)((char*)workspace + ws.pre_ml_off) : nullptr;
+    a.pre_o = prefix ? (float*)((char*)workspace + ws.pre_o_off) : nullptr;
+    a.pre_ml = prefix ? (float*)((char*)workspace + ws.pre_ml_off) : nullptr;
     a.k_res = int4 ? k_res : nullptr;
     a.v_res = int4 ? v_res : nullptr;
     a.extra_pieces = int4 ? 1 : 0;
@@ -406,11 +405,6 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     if (plan.stream) {
         e = launch_attn_mfma(a, s);
         if (e != hipSuccess) return hip_fail("attention launch", e);
-        if (int4) {
-            // the open blocks' residual-window tokens, one piece per row
-            e = launch_attn_residual(a, s);
-            if (e != hipSuccess) return hip_fail("residual attention launch", e);
-        }
         if (plan.split) {
             e = launch_merge_stream(a, s);
             if (e != hipSuccess) return hip_fail("merge launch", e);

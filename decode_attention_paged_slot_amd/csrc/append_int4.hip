@@ -35,45 +35,75 @@ __global__ void __launch_bounds__(64) k_append_int4(const uint16_t* __restrict__
                                                     int32_t max_blocks, int32_t num_blocks) {
     constexpr int EPL = HD / 64;   // new-row elements per lane
     constexpr int CPL = HD / 4;    // channels per lane when encoding
+    constexpr int V16 = CPL / 8;   // 16-B pieces per lane when encoding
+    __shared__ float kinv_sh[HD];
     const int w = blockIdx.x;
     const int b = w / n_kv, j = w - (w / n_kv) * n_kv;
     const int lane = threadIdx.x;
-    const int n = context_lens[b];
-    if (n <= 0 || n > max_blocks * 16) return;
-    const int t = n - 1, r = t & 15;
     const uint16_t* kn = k_new + (int64_t)w * HD;
     const uint16_t* vn = v_new + (int64_t)w * HD;
     uint16_t* kres = k_res + (int64_t)w * 16 * HD;
     uint16_t* vres = v_res + (int64_t)w * 16 * HD;
+    // Every load that does not depend on the row's length is issued first,
+    // together with it: the new row's elements this lane copies, the block's
+    // 16 rows this lane would encode (token tok = lane / 4, channels
+    // qq * CPL .. +CPL; token 15 is the new one, the others come from the
+    // residual buffer) and this lane's share of the key scales.
+    const int n = context_lens[b];
+    uint16_t kc[EPL], vc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-        kres[r * HD + EPL * lane + e] = kn[EPL * lane + e];
-        vres[r * HD + EPL * lane + e] = vn[EPL * lane + e];
+        kc[e] = kn[EPL * lane + e];
+        vc[e] = vn[EPL * lane + e];
     }
-    if (r != 15) return;
-    const int pb = block_table[(int64_t)b * max_blocks + t / 16];
-    if (pb < 0 || pb >= num_blocks) return;
-
     const int tok = lane >> 2, qq = lane & 3;
     const uint16_t* ksrc = (tok == 15 ? kn : kres + tok * HD) + qq * CPL;
     const uint16_t* vsrc = (tok == 15 ? vn : vres + tok * HD) + qq * CPL;
+    uint4 kw[V16], vw[V16];
+#pragma unroll
+    for (int v = 0; v < V16; ++v) {
+        kw[v] = *(const uint4*)(ksrc + 8 * v);
+        vw[v] = *(const uint4*)(vsrc + 8 * v);
+    }
+    float ks_l[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ks_l[e] = k_scale[(int64_t)j * HD + EPL * lane + e];
+    if (n <= 0 || n > max_blocks * 16) return;   // uniform per wave
+    const int t = n - 1, r = t & 15;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        kres[r * HD + EPL * lane + e] = kc[e];
+        vres[r * HD + EPL * lane + e] = vc[e];
+    }
+    if (r != 15) return;
+    const int pb = block_table[(int64_t)b * max_blocks + t / 16];
+    // fp32(1 / k_scale) of each channel, once per wave
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kinv_sh[EPL * lane + e] = __fdiv_rn(1.0f, ks_l[e]);
+    __syncthreads();
     float kx[CPL], vx[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        kx[c] = __uint_as_float((uint32_t)ksrc[c] << 16);
-        vx[c] = __uint_as_float((uint32_t)vsrc[c] << 16);
+    for (int v = 0; v < V16; ++v) {
+        const uint32_t ka[4] = {kw[v].x, kw[v].y, kw[v].z, kw[v].w};
+        const uint32_t va[4] = {vw[v].x, vw[v].y, vw[v].z, vw[v].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kx[8 * v + 2 * e] = bf16_lo_to_f32(ka[e]);
+            kx[8 * v + 2 * e + 1] = bf16_hi_to_f32(ka[e]);
+            vx[8 * v + 2 * e] = bf16_lo_to_f32(va[e]);
+            vx[8 * v + 2 * e + 1] = bf16_hi_to_f32(va[e]);
+        }
     }
     // keys, one scale per channel
-    const float* ks = k_scale + (int64_t)j * HD + qq * CPL;
     uint32_t kp[CPL / 8];
 #pragma unroll
     for (int gi = 0; gi < CPL / 8; ++gi) {
         uint32_t wv = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = quant_int4_nibble(__fmul_rn(kx[8 * gi + i], __fdiv_rn(1.0f, ks[8 * gi + i])));
-            const uint32_t hi =
-                quant_int4_nibble(__fmul_rn(kx[8 * gi + 4 + i], __fdiv_rn(1.0f, ks[8 * gi + 4 + i])));
+            const int c = qq * CPL + 8 * gi + i;
+            const uint32_t lo = quant_int4_nibble(__fmul_rn(kx[8 * gi + i], kinv_sh[c]));
+            const uint32_t hi = quant_int4_nibble(__fmul_rn(kx[8 * gi + 4 + i], kinv_sh[c + 4]));
             wv |= (lo | (hi << 4)) << (8 * i);
         }
         kp[gi] = wv;
@@ -106,6 +136,7 @@ __global__ void __launch_bounds__(64) k_append_int4(const uint16_t* __restrict__
         }
         vp[gi] = wv;
     }
+    if (pb < 0 || pb >= num_blocks) return;
     const int64_t row = ((int64_t)pb * n_kv + j) * 16 + tok;
     uint8_t* kd = k_q + row * (HD / 2) + qq * (CPL / 2);
     uint8_t* vd = v_q + row * (HD / 2) + qq * (CPL / 2);

@@ -337,7 +337,10 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             if (id < 0 || id >= a.num_blocks) id = -1;
             const int seg = b * n_kv + j;
             m.id = id;
-            m.info = ((pl > 0 || a.extra_pieces > 0) << 4) | ((bl == 0) << 5) | ((bl == nb - 1) << 6) |
+            // bit 4: the row's pieces always go to the merge (a shared
+            // prefix, or a 4-bit cache's non-empty residual window)
+            const bool merged = pl > 0 || (a.extra_pieces > 0 && (nn[b] & 15) != 0);
+            m.info = (merged << 4) | ((bl == 0) << 5) | ((bl == nb - 1) << 6) |
                      ((blk < a.reuse_blocks) << 7) | (seg << 8);
             m.mask = (int)block_token_mask(blk, nn[b], a.window, a.sinks);
             if (QUANT && id >= 0) {

@@ -67,10 +67,17 @@ struct PieceRuns {
     }
 };
 
+// An extra piece (xm, xl, xo) formed by the workgroup itself joins when
+// xl != 0: xm, xl are its statistics (the same in every thread) and xo this
+// thread's share of its unnormalised output sum_t 2^(s_t - xm) v_t over the
+// tokens of the thread's subset, for its column group; it enters with weight
+// xl 2^(xm - M) and output contribution 2^(xm - M) xo.
 template <int V>
 __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int c0,
                                           void* out_row, int32_t out_dtype, float* wsh,
-                                          float* red, f32x4* acc_sh) {
+                                          float* red, f32x4* acc_sh,
+                                          float xm = -__builtin_inff(), float xl = 0.0f,
+                                          f32x4 xo = f32x4{0.0f, 0.0f, 0.0f, 0.0f}) {
     constexpr int SUB = kThreads / V;  // partial subsets
     constexpr int KP = 4;              // partial outputs loaded ahead per thread
     const int np = pr.n1 + pr.n2;
@@ -84,13 +91,14 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
         const int p = min(sub + k * SUB, np - 1);
         ov[k] = np > 0 ? *((const f32x4*)pr.po(p) + c0 + c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    float mloc = -__builtin_inff();
+    float mloc = xl != 0.0f ? xm : -__builtin_inff();
     for (int p = threadIdx.x; p < np; p += kThreads) {
         const float2 x = *(const float2*)pr.ml(p);
         if (x.y != 0.0f) mloc = fmaxf(mloc, x.x);
     }
     const float M = block_max(mloc, red);
-    float lsum = 0.0f;
+    const float xs = xl != 0.0f ? __builtin_amdgcn_exp2f(xm - M) : 0.0f;
+    float lsum = threadIdx.x == 0 ? xl * xs : 0.0f;
     for (int p = threadIdx.x; p < np; p += kThreads) {
         const float2 x = *(const float2*)pr.ml(p);
         const float w = x.y == 0.0f ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
@@ -98,7 +106,7 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
         lsum += w;
     }
     const float L = block_sum(lsum, red);   // its barriers also publish wsh
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc = xs * xo;
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
         const int p = sub + k * SUB;
@@ -165,6 +173,92 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
     merge_row<HD / 4>(pr, row_bad, 0, orow, out_dtype, wsh, red, acc_sh);
 }
 
+// The residual window of a 4-bit cache as an extra piece of output row
+// `row` = b * n_q + h (SoK paper section 2.3: the newest tokens stay at full
+// precision until their group is quantized): its r = n % 16 newest tokens,
+// bf16 rows of k_res / v_res [B][n_kv][16][d_h], j = h / g. Thread tid forms
+// the partial dot product of q with k_t, t = tid / 16, over channels
+// (tid % 16) * d_h / 16 .. +d_h / 16; a 16-lane reduction gives the base-2
+// score s_t = scale * log2(e) * <q, k_t>, and the 16 scores pass through LDS
+// so that every thread forms m = max_t s_t and l = sum_t 2^(s_t - m) in the
+// same order. Thread (sub, c) then sums 2^(s_t - m) v_t over the tokens
+// t = sub, sub + SUB, ... for its column group c0 + c.
+template <int HD, int V>
+__device__ __forceinline__ void residual_piece(const AttnArgs& a, int64_t row, int b, int j,
+                                               int r, int c0, float* s_sh, float& xm,
+                                               float& xl, f32x4& xo) {
+    constexpr int SUB = kThreads / V;
+    constexpr int TPS = (16 + SUB - 1) / SUB;   // tokens per subset
+    constexpr int CP = HD / 16;                 // channels per thread in the scores
+    const int tid = threadIdx.x;
+    const int64_t rbase = ((int64_t)b * a.n_kv + j) * 16;   // residual rows of (b, j)
+    const uint16_t* kres = (const uint16_t*)a.k_res;
+    const uint16_t* vres = (const uint16_t*)a.v_res;
+    const int c = tid % V, sub = tid / V;
+    uint2 vw[TPS];
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) {
+        const int tt = sub + k * SUB;
+        vw[k] = tt < r ? *(const uint2*)(vres + (rbase + tt) * HD + 4 * (c0 + c))
+                       : make_uint2(0, 0);
+    }
+    const int t = tid >> 4, part = tid & 15;
+    float dot = 0.0f;
+    if (t < r) {
+        float kf[CP], qf[CP];
+        const uint16_t* kp = kres + (rbase + t) * HD + part * CP;
+        if constexpr (CP == 8) {
+            const uint4 w = *(const uint4*)kp;
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kf[2 * e] = bf16_lo_to_f32(ws[e]);
+                kf[2 * e + 1] = bf16_hi_to_f32(ws[e]);
+            }
+        } else {
+            const uint2 w = *(const uint2*)kp;
+            kf[0] = bf16_lo_to_f32(w.x); kf[1] = bf16_hi_to_f32(w.x);
+            kf[2] = bf16_lo_to_f32(w.y); kf[3] = bf16_hi_to_f32(w.y);
+        }
+        if (a.q_dtype == DT_BF16) {
+            const uint16_t* qp = (const uint16_t*)a.q + row * HD + part * CP;
+#pragma unroll
+            for (int e = 0; e < CP; ++e) qf[e] = __uint_as_float((uint32_t)qp[e] << 16);
+        } else {
+            const float* qp = (const float*)a.q + row * HD + part * CP;
+#pragma unroll
+            for (int e = 0; e < CP; ++e) qf[e] = qp[e];
+        }
+#pragma unroll
+        for (int e = 0; e < CP; ++e) dot += qf[e] * kf[e];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) dot += __shfl_xor(dot, o, 64);
+    if (part == 0) s_sh[t] = t < r ? dot * a.scale_log2 : -__builtin_inff();
+    __syncthreads();
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = fmaxf(m, s_sh[k]);
+    float l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) l += k < r ? __builtin_amdgcn_exp2f(s_sh[k] - m) : 0.0f;
+    f32x4 o4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) {
+        const int tt = sub + k * SUB;
+        if (tt < r) {
+            const float w = __builtin_amdgcn_exp2f(s_sh[tt] - m);
+            o4[0] += w * bf16_lo_to_f32(vw[k].x);
+            o4[1] += w * bf16_hi_to_f32(vw[k].x);
+            o4[2] += w * bf16_lo_to_f32(vw[k].y);
+            o4[3] += w * bf16_hi_to_f32(vw[k].y);
+        }
+    }
+    xm = m;
+    xl = l;
+    xo = o4;
+}
+
 // Stream layout (attention kernel's split mode): output row r = seg * g + hh
 // of segment seg; the pieces of a split segment sit in slots seg + w for the
 // waves w in seg_info[seg] = (first, last), piece row (seg + w) * g + hh.
@@ -172,8 +266,10 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
 // or none (zero / NaN rows, also written there) are skipped. With a shared
 // prefix (prefix_lens != nullptr), a row whose prefix has p blocks also has
 // the prefix pass's pieces of chunks 0 .. ceil(p / kPrefixChunk) - 1, at row
-// c * rows + r of pre_o / pre_ml, and its stream pieces always come here; a
-// 4-bit cache gives every row one extra piece there (its residual window).
+// c * rows + r of pre_o / pre_ml, and its stream pieces always come here. A
+// valid row of a 4-bit cache with n % 16 != 0 residual-window tokens has one
+// more piece, formed here from its bf16 residual rows (residual_piece), and
+// also always comes here.
 // With CS > 1 workgroups per row (grid.y), workgroup (row, cs) handles the
 // cs-th of CS column ranges, so rows with many pieces are spread over
 // several compute units. The weights live in dynamic LDS sized for the wave
@@ -184,25 +280,31 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
     extern __shared__ float wsh[];
     __shared__ float red[4];
     __shared__ f32x4 acc_sh[kThreads];
+    __shared__ float s_sh[16];
     const int64_t row = blockIdx.x;
     const int g = a.g;
     const int64_t seg = row / g;
     const int hh = (int)(row - seg * g);
     const int2 info = a.seg_info[seg];
     const int np = info.y - info.x + 1;
-    int npre = 0;
+    const int b = (int)(row / a.n_q);
+    int npre = 0, r_res = 0;
     if (a.prefix_lens != nullptr) {
-        const int b = (int)(row / a.n_q);
         const int pl = row_prefix_len(a.context_lens[b], a.prefix_lens[b], a.max_blocks,
                                       a.prefix_blocks);
         npre = pl > 0 ? (pl + kPrefixChunk - 1) / kPrefixChunk : 0;
-    } else if (a.extra_pieces > 0) {
-        // every valid row has its extra pieces (possibly empty); an invalid
-        // row keeps the NaN the attention kernel wrote
-        const int n = a.context_lens[row / a.n_q];
-        npre = (n >= 0 && n <= a.max_blocks * 16) ? a.extra_pieces : 0;
+    } else if (a.k_res != nullptr) {
+        // the residual window of a valid row; an invalid row keeps the NaN
+        // the attention kernel wrote
+        const int n = a.context_lens[b];
+        r_res = (n >= 0 && n <= a.max_blocks * 16) ? n % 16 : 0;
     }
-    if (npre == 0 && np <= 1) return;
+    if (npre == 0 && r_res == 0 && np <= 1) return;
+    const int c0 = (int)blockIdx.y * V;
+    float xm = -__builtin_inff(), xl = 0.0f;
+    f32x4 xo = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (r_res > 0)
+        residual_piece<HD, V>(a, row, b, (int)(seg % a.n_kv), r_res, c0, s_sh, xm, xl, xo);
     const int64_t prow0 = (seg + info.x) * g + hh;
     const int64_t rows = (int64_t)a.B * a.n_q;
     char* orow = (char*)a.out + row * HD * (a.out_dtype == DT_F32 ? 4 : 2);
@@ -210,7 +312,7 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
                        (int64_t)g * 2, max(np, 0),
                        npre ? a.pre_o + row * HD : nullptr, npre ? a.pre_ml + row * 2 : nullptr,
                        rows * HD, rows * 2, npre};
-    merge_row<V>(pr, false, (int)blockIdx.y * V, orow, a.out_dtype, wsh, red, acc_sh);
+    merge_row<V>(pr, false, c0, orow, a.out_dtype, wsh, red, acc_sh, xm, xl, xo);
 }
 
 hipError_t launch_merge(const float* part_o, const float* part_ml, const int32_t* context_lens,
@@ -237,7 +339,7 @@ hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.n_q;
     if (rows == 0) return hipSuccess;
     const int chunks = a.prefix_blocks > 0 ? (a.prefix_blocks + kPrefixChunk - 1) / kPrefixChunk
-                                           : a.extra_pieces;
+                                           : 0;
     const size_t lds = (size_t)(a.nw + chunks) * sizeof(float);
     // split a row's columns over several workgroups only when segments
     // average many pieces (long sequences in a small batch)

@@ -81,15 +81,14 @@ struct AttnArgs {
     float* pre_ml;   // [chunks][B * n_q][2]
     // 4-bit cache (kv_dtype DT_INT4): k_scale is [n_kv][d_h] (per channel),
     // v_scale [num_blocks][n_kv][16] (per token); each row's open block is in
-    // k_res / v_res [B][n_kv][16][d_h] bf16, attended as one extra piece per
-    // output row (extra_pieces = 1, written to pre_o / pre_ml chunk 0)
+    // k_res / v_res [B][n_kv][16][d_h] bf16 (extra_pieces = 1): the merge
+    // attends it as one more piece of every row with n % 16 != 0
     const void* k_res;
     const void* v_res;
     int32_t extra_pieces;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_residual(const AttnArgs& a, hipStream_t s);
 hipError_t launch_append_int4(const void* k_new, const void* v_new, const int32_t* block_table,
                               const int32_t* context_lens, void* k_q, void* v_q,
                               const float* k_scale, float* v_scale, void* k_res, void* v_res,
