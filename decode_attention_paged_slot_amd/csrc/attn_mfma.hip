@@ -499,6 +499,14 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 
     auto ksc_of = [&](int i) { return QUANT ? meta_f(A.ksc, Bm.ksc, i) : 1.0f; };
     auto vsc_of = [&](int i) { return QUANT ? meta_f(A.vsc, Bm.vsc, i) : 1.0f; };
+    // the consumed block always lies in batch A (the consumer moves to the
+    // next batch first), so its fields need no batch select
+    auto cur_id = [&](int i) { return __builtin_amdgcn_readlane(A.id, i & 63); };
+    auto cur_info = [&](int i) { return __builtin_amdgcn_readlane(A.info, i & 63); };
+    auto cur_mask = [&](int i) { return (uint32_t)__builtin_amdgcn_readlane(A.mask, i & 63); };
+    auto cur_f = [&](float f, int i) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), i & 63));
+    };
 
     uint4 kr[kDepth][T::LOADS], vr[kDepth][T::LOADS];
     f32x4 vsr[kDepth];   // 4-bit: value scales of this lane's 4 tokens
@@ -611,8 +619,8 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             ++batchA;
             if ((batchA + 1) * 64 < cnt) Bm = load_meta(batchA + 1);
         }
-        const int info = meta_info(i);
-        const uint32_t mask = meta_mask(i);
+        const int info = cur_info(i);
+        const uint32_t mask = cur_mask(i);
         const bool seg_first = (info >> 5) & 1;
         const bool seg_last = (info >> 6) & 1;
         const int seg = (int)((unsigned)info >> 8);
@@ -634,11 +642,11 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         }
         // 4-bit value scales of this block, taken before the slot is refilled
         const f32x4 vsb = I4 ? vsr[s] : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-        const int pb_i = meta_id(i);
+        const int pb_i = cur_id(i);
         // block scales, read while every lane is active (a readlane inside a
         // divergent branch would read an unselected lane's stale register)
-        const float ksc = ksc_of(i);
-        const float vsc = vsc_of(i);
+        const float ksc = QUANT ? cur_f(A.ksc, i) : 1.0f;
+        const float vsc = QUANT ? cur_f(A.vsc, i) : 1.0f;
         if (pb_i < 0) piece_bad = true;
         if (!I4 && a.k_new != nullptr && seg_last && pb_i >= 0) {
             // fused decode step: this block holds the row's newest position

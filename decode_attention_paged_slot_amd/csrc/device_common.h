@@ -69,7 +69,8 @@ __device__ __forceinline__ int32_t quant_int8(float y) {
 
 // Two fp32 values holding exact bf16 values -> packed bf16x2 (lo, hi).
 __device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    // bytes 2, 3 of lo, then bytes 2, 3 of hi: one v_perm_b32
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // 4 fp8 codes (one dword) -> 4 bf16 (two dwords), exact.
