@@ -123,6 +123,30 @@ def test_int4_attention_matches_oracle(d_h, n_q, n_kv, qd, nw):
     assert (got[0] == 0).all()   # empty row
 
 
+@pytest.mark.parametrize("d_h", [128, 64])
+@pytest.mark.parametrize("n", [4001, 4015, 4096])
+def test_int4_column_split_merge(d_h, n):
+    """One long row over 128 waves: the merge splits the row's columns over
+    several workgroups, each forming its own share of the residual piece
+    (residual windows of 1, 15 and no tokens)."""
+    print(f"int4 column-split merge d_h={d_h} n={n}", flush=True)
+    sys.stdout.flush()
+    st, ks, table, ctx, nb, mb = _case(5400 + d_h + n, [n], n_q=8, n_kv=1, d_h=d_h)
+    r = np.random.default_rng(12)
+    q_np = synth.gaussian((1, 8, d_h), BF16, r)
+    st_d, ks_d = _dev(st, ks, "cuda")
+    scale = 1.0 / np.sqrt(d_h)
+    desc = _desc(1, 8, 1, d_h, mb, nb, BF16, F32, ctx, 128)
+    import decode_attention_paged_slot_amd as pda
+    assert pda.attn_plan(desc)[0] == 128   # 128 waves for one (row, head) segment
+    got = _attend(st_d, ks_d, to_dev(q_np, BF16, "cuda"), table, ctx, scale, desc)
+    ref, _, _, bad = oracle.paged_attn_int4(q_np, st, ks, table, ctx, scale, n_q=8, n_kv=1,
+                                            q_dtype=BF16)
+    assert bad == 0
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - ref.reshape(got.shape)).max()) < TOL_8BIT
+
+
 def test_int4_bf16_output_and_invalid_rows():
     import torch
     st, ks, table, ctx, nb, mb = _case(5100, [300, 17, 40, 5, 64], n_q=8, n_kv=2, d_h=128)
