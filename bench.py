@@ -76,6 +76,11 @@ def parse_args(argv=None):
     ap.add_argument("--graph", dest="graph", action="store_true", default=False,
                     help="replay the step from a captured HIP graph (eager launches by "
                          "default: on this stack a replay adds ~6 us per step)")
+    ap.add_argument("--sweep", action="store_true", default=False,
+                    help="also time the attention call at 1/4, 1/2 and 2x the workload's "
+                         "context lengths and fit us = fixed + bytes / rate: the kernel's "
+                         "steady streaming rate apart from its fixed per-call cost (workloads "
+                         "whose bytes scale with context: no window, shared prefix or 4-bit)")
     return ap.parse_args(argv)
 
 
@@ -94,6 +99,58 @@ def build_inputs(w, dev):
     synth.apply_sinks_device(w, inp, table)
     synth.poison_unowned_device(w, inp, table)
     return inp, pool, shared, table, slots
+
+
+def context_sweep(w, dev, reps, factors=(0.25, 0.5, 2.0)):
+    """Attention-call time at scaled context lengths of workload `w` (same
+    shape, seed and structure otherwise): [(factor, attention bytes, us)].
+    Each point is the median of 5 runs of `reps` back-to-back calls between
+    two HIP events on the launch stream."""
+    import torch
+    import synth
+    import decode_attention_paged_slot_amd as pda
+    from decode_attention_paged_slot_amd import accounting as acc
+
+    pts = []
+    for f in factors:
+        w2 = w.with_(ctx_lo=max(1, int(round(w.ctx_lo * f))), ctx_hi=max(1, int(round(w.ctx_hi * f))))
+        inp, pool, _, table, _ = build_inputs(w2, dev)
+        bt = torch.from_numpy(table).to(dev)
+        cl = torch.from_numpy(inp.ctx).to(dev)
+        out = torch.empty((w2.B, w2.n_q, w2.d_h), dtype=torch.float32, device=dev)
+        desc = pda.attn_desc(inp.q, inp.k_cache, bt, max_context=int(inp.ctx.max()),
+                             kv_dtype=w2.kv_dtype, total_context=int(inp.ctx.sum()))
+        ws = pda.workspace_for(desc, dev)
+        if w2.kv_dtype in (synth.FP8, synth.INT8):
+            def call():
+                pda.paged_decode_attn_quant(inp.q, inp.k_cache, inp.v_cache, inp.k_scale,
+                                            inp.v_scale, bt, cl, w2.softmax_scale, out,
+                                            desc=desc, workspace=ws)
+        else:
+            def call():
+                pda.paged_decode_attn(inp.q, inp.k_cache, inp.v_cache, bt, cl,
+                                      w2.softmax_scale, out, desc=desc, workspace=ws)
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / reps)
+        nbytes = acc.step_bytes(inp.ctx, n_q=w2.n_q, n_kv=w2.n_kv, d_h=w2.d_h,
+                                block_size=w2.block_size, kv_dtype=w2.kv_dtype,
+                                q_dtype=w2.q_dtype, new_dtype=synth.BF16).attention
+        pts.append((f, int(nbytes), float(np.median(per))))
+        _say(f"[bench] sweep x{f}: {nbytes / 1e9:.3f} GB in {pts[-1][2]:.2f} us")
+        pool.close()
+        del inp, bt, cl, out, ws
+        torch.cuda.empty_cache()
+    return pts
 
 
 def oracle_leg(w, inp, table, slots, shared, host):
@@ -458,6 +515,20 @@ def main(argv=None) -> int:
 
     probe = None if args.no_probe else stream_probe(dev)
 
+    steady = None
+    if args.sweep and not (int4 or w.attn_window or inp.shared_ids_count):
+        pts = context_sweep(w, dev, K) + [(1.0, int(sb.attention), att_avg * 1e3)]
+        pts.sort()
+        x = np.array([p[1] for p in pts], dtype=np.float64) / 1e9
+        y = np.array([p[2] for p in pts], dtype=np.float64)
+        slope, icpt = np.polyfit(x, y, 1)   # us per GB, us
+        steady = {"GBps": round(1e6 / slope, 1), "frac": round(1e6 / slope / HBM_PEAK_GBPS, 4),
+                  "fixed_us": round(float(icpt), 2),
+                  "points": [{"context_scale": f, "bytes": b, "us": round(u, 2)}
+                             for f, b, u in pts],
+                  "fit": "least squares us = fixed_us + bytes / GBps over the points"}
+        _say(f"[bench] sweep fit: steady {steady['GBps']:.0f} GB/s, fixed {icpt:.2f} us per call")
+
     res = {
         "metric": "decode-attn KV GB/s (% MI355X HBM peak) + us/step, 70B-shape batch 8x32k",
         "value": round(value, 2),
@@ -510,6 +581,7 @@ def main(argv=None) -> int:
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(w.name)},
         "stream_scale_copy_probe_GBps": None if probe is None else round(probe, 1),
+        **({} if steady is None else {"steady_state": steady}),
         "parity": parity,
         "cpu_baseline": cpu,
     }
