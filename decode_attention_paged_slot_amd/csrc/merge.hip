@@ -7,9 +7,12 @@
 // out. The split keeps the single cache read and the no-score-spill property
 // of the attention step (SoK paper appendices A.1, C.4).
 //
-// One workgroup per output row: a block-wide max and sum over the partials'
-// statistics, then a weighted sum of the partial outputs split over
-// partition subsets, combined through LDS.
+// Two forms. Rows with few pieces and no extra (prefix or residual) pieces:
+// one wave per output row, every load in flight at once, wave reductions
+// only (k_merge_rows). Otherwise one workgroup per output row (or per column
+// slice of it): a block-wide max and sum over the partials' statistics, then
+// a weighted sum of the partial outputs split over partition subsets,
+// combined through LDS (merge_row).
 #include "device_common.h"
 #include "pda_internal.h"
 
@@ -315,6 +318,89 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
     merge_row<V>(pr, false, c0, orow, a.out_dtype, wsh, red, acc_sh, xm, xl, xo);
 }
 
+// Stream layout with only the stream pieces (no shared-prefix pieces, no
+// residual window) and few pieces per row: one wave per output row. Pieces
+// are taken in batches of up to 32: lane l holds the statistics of piece
+// p0 + l, and the partial outputs of its float4 column c = l % C (C = d_h / 4
+// columns) for pieces p0 + h, p0 + h + H, ... (h = l / C, H = 64 / C). All
+// of a batch's loads are issued before any is used; the batch max and weight
+// sum are wave reductions, a piece's weight reaches the lanes holding its
+// output by a lane shuffle, and the H partial sums of a column meet by lane
+// exchanges: no LDS, no barrier. A later batch rescales the running sums to
+// the new max. As in merge_row, a piece with l_p = 0 drops out and a NaN l_p
+// (a piece that met an unmapped block) makes the row NaN.
+template <int HD>
+__global__ void __launch_bounds__(kThreads) k_merge_rows(AttnArgs a) {
+    constexpr int C = HD / 4;    // float4 columns of a row
+    constexpr int H = 64 / C;    // lanes per column
+    constexpr int KB = 32;       // pieces per batch
+    constexpr int PL = KB / H;   // pieces per lane and batch
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.B * a.n_q) return;
+    const int g = a.g;
+    const int64_t seg = row / g;
+    const int hh = (int)(row - seg * g);
+    const int2 info = a.seg_info[seg];
+    const int np = info.y - info.x + 1;
+    // a single piece was written to the output by the attention kernel, and
+    // so were the zero / NaN rows of empty or invalid sequences (np = 0)
+    if (np <= 1) return;
+    const int64_t prow0 = (seg + info.x) * g + hh;   // piece p: piece row prow0 + p * g
+    const int c = lane % C, h = lane / C;
+    float M = -__builtin_inff(), L = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = 0; p0 < np; p0 += KB) {
+        const int nb = min(KB, np - p0);
+        f32x4 ov[PL];
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const int p = h + H * k;
+            ov[k] = p < nb ? *((const f32x4*)(a.part_o + (prow0 + (int64_t)(p0 + p) * g) * HD) + c)
+                           : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        float2 st = make_float2(0.0f, 0.0f);
+        if (lane < nb) st = *(const float2*)(a.part_ml + (prow0 + (int64_t)(p0 + lane) * g) * 2);
+        float mb = st.y != 0.0f ? st.x : -__builtin_inff();
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+        const float Mn = fmaxf(M, mb);
+        const float w = st.y == 0.0f ? 0.0f : st.y * __builtin_amdgcn_exp2f(st.x - Mn);
+        float lb = w;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lb += __shfl_xor(lb, o, 64);
+        const float f = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+        acc *= f;
+        L = L * f + lb;
+        M = Mn;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const float wk = __shfl(w, h + H * k, 64);
+            if (wk != 0.0f) acc += wk * ov[k];
+        }
+    }
+#pragma unroll
+    for (int o = C; o < 64; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o, 64);
+        acc.y += __shfl_xor(acc.y, o, 64);
+        acc.z += __shfl_xor(acc.z, o, 64);
+        acc.w += __shfl_xor(acc.w, o, 64);
+    }
+    if (h == 0) {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = L != 0.0f ? acc[e] / L : 0.0f;
+        if (a.out_dtype == DT_F32) {
+            *((f32x4*)((float*)a.out + row * HD) + c) = r;
+        } else {
+            uint2 o2;
+            o2.x = f32_to_bf16_rne(r[0]) | (f32_to_bf16_rne(r[1]) << 16);
+            o2.y = f32_to_bf16_rne(r[2]) | (f32_to_bf16_rne(r[3]) << 16);
+            *((uint2*)((uint16_t*)a.out + row * HD) + c) = o2;
+        }
+    }
+}
+
 hipError_t launch_merge(const float* part_o, const float* part_ml, const int32_t* context_lens,
                         int32_t rows, int32_t n_q, int32_t P, int32_t bpp, int32_t max_blocks,
                         int32_t d_h, void* out, int32_t out_dtype, hipStream_t s) {
@@ -344,6 +430,15 @@ hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s) {
     // split a row's columns over several workgroups only when segments
     // average many pieces (long sequences in a small batch)
     const bool wide = (int64_t)a.nw >= 64 * (int64_t)a.B * a.n_kv;
+    if (!wide && a.prefix_lens == nullptr && a.k_res == nullptr) {
+        // only stream pieces, few per row: one wave per row. (Rows with many
+        // pieces keep the block-wide merge: split over column slices, waves
+        // per row measured slower there, with fewer loads in flight.)
+        const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64)));
+        if (a.d_h == 128) hipLaunchKernelGGL((k_merge_rows<128>), grid, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((k_merge_rows<64>), grid, dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
 #define PDA_MS(HD, CS)                                                                       \
     hipLaunchKernelGGL((k_merge_stream<HD, CS>), dim3(rows, CS), dim3(kThreads), lds, s, a)
     if (a.d_h == 128) {

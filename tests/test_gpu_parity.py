@@ -374,3 +374,46 @@ def test_lse_merge_matches_oracle_merge():
     torch.cuda.synchronize()
     assert max_err(out.cpu().numpy(), ref) < 1e-5
     assert max_err(out.cpu().numpy(), c.oracle_out().reshape(rows, -1)) < 1e-5
+
+
+# ------------------------------------------------------------------- merge
+@pytest.mark.parametrize("d_h", [64, 128])
+@pytest.mark.parametrize("out_dtype", [F32, BF16])
+def test_merge_many_pieces_per_row(d_h, out_dtype):
+    """One long row split into ~1000 pieces: the merge takes its pieces in
+    several batches (rescaling between them), over column slices of a row."""
+    c = make_case(8100 + d_h + out_dtype, [20000], n_q=4, n_kv=1, d_h=d_h)
+    _say(f"merge many pieces d_h={d_h} out={out_dtype}")
+    got, _ = run_case(c, num_partitions=1000, out_dtype=out_dtype)
+    ref = c.oracle_out()
+    tol = TOL_16BIT if out_dtype == F32 else 2e-2   # bf16 output: half an ulp at |x| < 4
+    assert max_err(got, ref) < tol
+
+
+@pytest.mark.parametrize("d_h", [64, 128])
+@pytest.mark.parametrize("nw", [200, 2047])
+def test_merge_one_long_row_among_short(d_h, nw):
+    """A long row among short ones: its segments take most of the wave ranges
+    (far more pieces than the average the merge is laid out for), the short
+    rows one or two pieces each."""
+    ctx = [100] * 16
+    ctx[5] = 30000
+    ctx[11] = 3
+    c = make_case(8200 + d_h + nw, ctx, n_q=8, n_kv=2, d_h=d_h)
+    _say(f"merge long row among short d_h={d_h} nw={nw}")
+    got, _ = run_case(c, num_partitions=nw)
+    assert max_err(got, c.oracle_out()) < TOL_16BIT
+
+
+@pytest.mark.parametrize("nw", [7, 1000])
+def test_merge_nan_piece_poisons_row(nw):
+    """An unmapped block inside a split row: its piece carries a NaN sum, and
+    the merged row must be NaN while the other rows stay exact."""
+    c = make_case(8300 + nw, [5000, 4000, 3000], n_q=8, n_kv=2, d_h=128)
+    t = c.table.copy()
+    t[1, 100] = -1
+    _say(f"merge nan piece nw={nw}")
+    got, _ = run_case(c, table=t, num_partitions=nw)
+    ref = c.oracle_out()
+    assert np.isnan(got[1]).all()
+    assert max_err(got[[0, 2]], ref[[0, 2]]) < TOL_16BIT
