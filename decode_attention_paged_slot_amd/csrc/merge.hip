@@ -74,13 +74,22 @@ struct PieceRuns {
 // xl != 0: xm, xl are its statistics (the same in every thread) and xo this
 // thread's share of its unnormalised output sum_t 2^(s_t - xm) v_t over the
 // tokens of the thread's subset, for its column group; it enters with weight
-// xl 2^(xm - M) and output contribution 2^(xm - M) xo.
-template <int V>
+// xl 2^(xm - M) and output contribution 2^(xm - M) xo. `extra(xm, xl, xo)`
+// forms it (every thread calls it); it runs after the first partial outputs
+// and statistics have been requested, so its own loads share their round
+// trip.
+struct NoExtraPiece {
+    __device__ __forceinline__ void operator()(float& xm, float& xl, f32x4& xo) const {
+        xm = -__builtin_inff();
+        xl = 0.0f;
+        xo = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+};
+
+template <int V, class Extra>
 __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int c0,
                                           void* out_row, int32_t out_dtype, float* wsh,
-                                          float* red, f32x4* acc_sh,
-                                          float xm = -__builtin_inff(), float xl = 0.0f,
-                                          f32x4 xo = f32x4{0.0f, 0.0f, 0.0f, 0.0f}) {
+                                          float* red, f32x4* acc_sh, Extra extra) {
     constexpr int SUB = kThreads / V;  // partial subsets
     constexpr int KP = 4;              // partial outputs loaded ahead per thread
     const int np = pr.n1 + pr.n2;
@@ -94,15 +103,27 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
         const int p = min(sub + k * SUB, np - 1);
         ov[k] = np > 0 ? *((const f32x4*)pr.po(p) + c0 + c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // this thread's first statistics (piece threadIdx.x), in flight with them
+    const bool has0 = (int)threadIdx.x < np;
+    const float2 x0 = has0 ? *(const float2*)pr.ml(threadIdx.x) : make_float2(0.0f, 0.0f);
+    float xm, xl;
+    f32x4 xo;
+    extra(xm, xl, xo);
     float mloc = xl != 0.0f ? xm : -__builtin_inff();
-    for (int p = threadIdx.x; p < np; p += kThreads) {
+    if (has0 && x0.y != 0.0f) mloc = fmaxf(mloc, x0.x);
+    for (int p = threadIdx.x + kThreads; p < np; p += kThreads) {
         const float2 x = *(const float2*)pr.ml(p);
         if (x.y != 0.0f) mloc = fmaxf(mloc, x.x);
     }
     const float M = block_max(mloc, red);
     const float xs = xl != 0.0f ? __builtin_amdgcn_exp2f(xm - M) : 0.0f;
     float lsum = threadIdx.x == 0 ? xl * xs : 0.0f;
-    for (int p = threadIdx.x; p < np; p += kThreads) {
+    if (has0) {
+        const float w = x0.y == 0.0f ? 0.0f : x0.y * __builtin_amdgcn_exp2f(x0.x - M);
+        wsh[threadIdx.x] = w;
+        lsum += w;
+    }
+    for (int p = threadIdx.x + kThreads; p < np; p += kThreads) {
         const float2 x = *(const float2*)pr.ml(p);
         const float w = x.y == 0.0f ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
         wsh[p] = w;
@@ -173,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
     char* orow = (char*)out + row * HD * (out_dtype == DT_F32 ? 4 : 2);
     const PieceRuns pr{part_o + row * (int64_t)P * HD, part_ml + row * (int64_t)P * 2, HD, 2, np,
                        nullptr, nullptr, 0, 0, 0};
-    merge_row<HD / 4>(pr, row_bad, 0, orow, out_dtype, wsh, red, acc_sh);
+    merge_row<HD / 4>(pr, row_bad, 0, orow, out_dtype, wsh, red, acc_sh, NoExtraPiece{});
 }
 
 // The residual window of a 4-bit cache as an extra piece of output row
@@ -304,10 +325,6 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
     }
     if (npre == 0 && r_res == 0 && np <= 1) return;
     const int c0 = (int)blockIdx.y * V;
-    float xm = -__builtin_inff(), xl = 0.0f;
-    f32x4 xo = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (r_res > 0)
-        residual_piece<HD, V>(a, row, b, (int)(seg % a.n_kv), r_res, c0, s_sh, xm, xl, xo);
     const int64_t prow0 = (seg + info.x) * g + hh;
     const int64_t rows = (int64_t)a.B * a.n_q;
     char* orow = (char*)a.out + row * HD * (a.out_dtype == DT_F32 ? 4 : 2);
@@ -315,7 +332,15 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
                        (int64_t)g * 2, max(np, 0),
                        npre ? a.pre_o + row * HD : nullptr, npre ? a.pre_ml + row * 2 : nullptr,
                        rows * HD, rows * 2, npre};
-    merge_row<V>(pr, false, c0, orow, a.out_dtype, wsh, red, acc_sh, xm, xl, xo);
+    // the residual window's piece is formed once the stored pieces' loads
+    // are in flight
+    merge_row<V>(pr, false, c0, orow, a.out_dtype, wsh, red, acc_sh,
+                 [&](float& xm, float& xl, f32x4& xo) {
+                     NoExtraPiece{}(xm, xl, xo);
+                     if (r_res > 0)
+                         residual_piece<HD, V>(a, row, b, (int)(seg % a.n_kv), r_res, c0, s_sh,
+                                               xm, xl, xo);
+                 });
 }
 
 // Stream layout with only the stream pieces (no shared-prefix pieces, no
