@@ -23,14 +23,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMergeColumnSplit = 4;   // workgroups per output row when segments have many pieces
 
+// Block-wide max and sum of a 4-wave workgroup. Each takes its own 4-float
+// LDS slot (`red`) and is used once per workgroup, so no barrier is needed
+// after the slot is read.
 __device__ __forceinline__ float block_max(float v, float* red) {
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
-    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    return v;
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -38,9 +39,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
-    v = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
-    return v;
+    return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // Merge of the partials of one output row into `out_row` (HD floats or
@@ -115,7 +114,7 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
         const float2 x = *(const float2*)pr.ml(p);
         if (x.y != 0.0f) mloc = fmaxf(mloc, x.x);
     }
-    const float M = block_max(mloc, red);
+    const float M = block_max(mloc, red);   // red[0..3]
     const float xs = xl != 0.0f ? __builtin_amdgcn_exp2f(xm - M) : 0.0f;
     float lsum = threadIdx.x == 0 ? xl * xs : 0.0f;
     if (has0) {
@@ -129,7 +128,7 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
         wsh[p] = w;
         lsum += w;
     }
-    const float L = block_sum(lsum, red);   // its barriers also publish wsh
+    const float L = block_sum(lsum, red + 4);   // its barrier also publishes wsh
     f32x4 acc = xs * xo;
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
@@ -145,12 +144,21 @@ __device__ __forceinline__ void merge_row(const PieceRuns& pr, bool row_bad, int
         const float w = wsh[p];
         if (w != 0.0f) acc += w * o;
     }
-    acc_sh[sub * V + c] = acc;
+    // the SUB subset sums of a column: within a wave they sit in lanes c,
+    // c + V, ... and add by lane exchanges; the four waves' sums meet in LDS
+    static_assert(64 % V == 0 && kThreads == 256, "column groups tile a wave");
+#pragma unroll
+    for (int o = V; o < 64; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o, 64);
+        acc.y += __shfl_xor(acc.y, o, 64);
+        acc.z += __shfl_xor(acc.z, o, 64);
+        acc.w += __shfl_xor(acc.w, o, 64);
+    }
+    const int wv = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) < V) acc_sh[wv * V + c] = acc;
     __syncthreads();
     if (sub == 0) {
-        f32x4 tot = acc_sh[c];
-#pragma unroll
-        for (int k = 1; k < SUB; ++k) tot += acc_sh[k * V + c];
+        const f32x4 tot = (acc_sh[c] + acc_sh[V + c]) + (acc_sh[2 * V + c] + acc_sh[3 * V + c]);
         f32x4 r;
         const bool ok = L != 0.0f;
 #pragma unroll
@@ -180,7 +188,7 @@ __global__ void __launch_bounds__(kThreads) k_merge(const float* __restrict__ pa
                                                     int32_t max_blocks, void* out,
                                                     int32_t out_dtype) {
     __shared__ float wsh[kMaxPartitions];
-    __shared__ float red[4];
+    __shared__ float red[8];   // block_max, block_sum
     __shared__ f32x4 acc_sh[kThreads];
     const int64_t row = blockIdx.x;
     int np = P;
@@ -302,7 +310,7 @@ template <int HD, int CS>
 __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
     constexpr int V = HD / 4 / CS;
     extern __shared__ float wsh[];
-    __shared__ float red[4];
+    __shared__ float red[8];   // block_max, block_sum
     __shared__ f32x4 acc_sh[kThreads];
     __shared__ float s_sh[16];
     const int64_t row = blockIdx.x;
