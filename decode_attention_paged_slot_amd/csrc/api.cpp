@@ -268,16 +268,32 @@ int32_t check_attn_desc(const pda_attn_desc* d, CallKind kind) {
     return PDA_OK;
 }
 
-// PDA_DEBUG: validate block table and lengths on the host before launching.
+// PDA_DEBUG: validate lengths and table entries on the host before launching,
+// by the rule the kernels follow: a row is invalid if its length is outside
+// [0, max_blocks * bs] or a block it looks up is unmapped (outside
+// [0, num_blocks)). Looked up are, with a sliding window, only the sink
+// blocks and the window's blocks; with a shared prefix of pl blocks, the
+// prefix table's first pl entries instead of the row's own (and pl must be
+// below the row's block count); with a 4-bit cache, the n / 16 encoded
+// blocks (the open block is in the residual buffer).
 int32_t debug_check(const pda_attn_desc* d, const int32_t* block_table,
-                    const int32_t* context_lens, hipStream_t s) {
+                    const int32_t* context_lens, const int32_t* prefix_table,
+                    const int32_t* prefix_lens, bool int4, hipStream_t s) {
+    const bool prefix = prefix_table != nullptr;
     std::vector<int32_t> lens((size_t)d->B), table((size_t)d->B * d->max_blocks_per_seq);
+    std::vector<int32_t> plens(prefix ? (size_t)d->B : 0), ptable(prefix ? (size_t)d->prefix_blocks : 0);
     hipError_t e = hipMemcpyAsync(lens.data(), context_lens, lens.size() * 4,
                                   hipMemcpyDeviceToHost, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(table.data(), block_table, table.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && prefix)
+        e = hipMemcpyAsync(plens.data(), prefix_lens, plens.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && prefix)
+        e = hipMemcpyAsync(ptable.data(), prefix_table, ptable.size() * 4, hipMemcpyDeviceToHost,
+                           s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail("PDA_DEBUG copy", e);
+    const int32_t sinks = d->window > 0 ? d->sink_tokens : 0;
     for (int32_t b = 0; b < d->B; ++b) {
         const int32_t n = lens[(size_t)b];
         if (n < 0 || (int64_t)n > (int64_t)d->max_blocks_per_seq * kBlockSize) {
@@ -285,7 +301,32 @@ int32_t debug_check(const pda_attn_desc* d, const int32_t* block_table,
                       (long long)d->max_blocks_per_seq * kBlockSize);
             return PDA_EINVAL;
         }
-        for (int32_t i = 0; i < (n + kBlockSize - 1) / kBlockSize; ++i) {
+        const int32_t nblk = (n + kBlockSize - 1) / kBlockSize;
+        int32_t pl = 0;
+        if (prefix && n > 0) {
+            pl = plens[(size_t)b];
+            if (pl < 0 || pl > d->prefix_blocks || pl >= nblk) {
+                set_error("row %d: shared-prefix length %d outside [0, min(%d, %d)]", b, pl,
+                          d->prefix_blocks, nblk - 1);
+                return PDA_EINVAL;
+            }
+            for (int32_t i = 0; i < pl; ++i) {
+                const int32_t pb = ptable[(size_t)i];
+                if (pb < 0 || pb >= d->num_blocks) {
+                    set_error("row %d: shared-prefix block %d is unmapped (entry %d)", b, i, pb);
+                    return PDA_EINVAL;
+                }
+            }
+        }
+        // attended blocks: all, or the sink blocks and those from the window's start
+        int32_t sb = nblk, wstart = nblk;
+        if (d->window > 0 && n > sinks + d->window) {
+            sb = (sinks + kBlockSize - 1) / kBlockSize;
+            wstart = std::max((n - d->window) / kBlockSize, sb);
+        }
+        const int32_t last = int4 ? n / kBlockSize : nblk;
+        for (int32_t i = pl; i < last; ++i) {
+            if (i >= sb && i < wstart) continue;
             const int32_t pb = table[(size_t)b * d->max_blocks_per_seq + i];
             if (pb < 0 || pb >= d->num_blocks) {
                 set_error("row %d: logical block %d is unmapped (entry %d)", b, i, pb);
@@ -343,7 +384,8 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     }
     hipStream_t s = (hipStream_t)stream;
     if (debug_mode()) {
-        rc = debug_check(d, block_table, context_lens, s);
+        rc = debug_check(d, block_table, context_lens, kind == kPrefix ? prefix_table : nullptr,
+                         prefix_lens, kind == kInt4, s);
         if (rc != PDA_OK) return rc;
     }
     AttnArgs a{};

@@ -254,7 +254,10 @@ int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
  * Rows may share physical blocks (read-only aliasing). Errors: EINVAL,
  * EWORKSPACE, EHIP. With PDA_DEBUG=1 in the environment the host also copies
  * block_table / context_lens back (synchronising `stream`) and returns EINVAL
- * for any such row before launching. */
+ * for any such row before launching. It checks the blocks the call looks up,
+ * as the kernels do: blocks a sliding window skips are not looked up (nor,
+ * in the _prefix calls, a row's own entries below its prefix length, nor, in
+ * the _int4 calls, a row's open block). */
 int32_t pda_paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* context_lens, float scale,
                               void* out, const pda_attn_desc* d, void* workspace,
