@@ -7,9 +7,9 @@
 // out. The split keeps the single cache read and the no-score-spill property
 // of the attention step (SoK paper appendices A.1, C.4).
 //
-// Two forms. Rows with few pieces and no extra (prefix or residual) pieces:
-// one wave per output row, every load in flight at once, wave reductions
-// only (k_merge_rows). Otherwise one workgroup per output row (or per column
+// Two forms. Rows with few pieces and no residual-window piece: one wave per
+// output row, every load in flight at once, wave reductions only
+// (k_merge_rows). Otherwise one workgroup per output row (or per column
 // slice of it): a block-wide max and sum over the partials' statistics, then
 // a weighted sum of the partial outputs split over partition subsets,
 // combined through LDS (merge_row).
@@ -351,9 +351,10 @@ __global__ void __launch_bounds__(kThreads) k_merge_stream(AttnArgs a) {
                  });
 }
 
-// Stream layout with only the stream pieces (no shared-prefix pieces, no
-// residual window) and few pieces per row: one wave per output row. Pieces
-// are taken in batches of up to 32: lane l holds the statistics of piece
+// Stream layout without a residual window and with few pieces per row: one
+// wave per output row. A row's pieces are its stream pieces, then (with a
+// shared prefix) the prefix pass's pieces of its prefix chunks. Pieces are
+// taken in batches of up to 32: lane l holds the statistics of piece
 // p0 + l, and the partial outputs of its float4 column c = l % C (C = d_h / 4
 // columns) for pieces p0 + h, p0 + h + H, ... (h = l / C, H = 64 / C). All
 // of a batch's loads are issued before any is used; the batch max and weight
@@ -375,11 +376,30 @@ __global__ void __launch_bounds__(kThreads) k_merge_rows(AttnArgs a) {
     const int64_t seg = row / g;
     const int hh = (int)(row - seg * g);
     const int2 info = a.seg_info[seg];
-    const int np = info.y - info.x + 1;
-    // a single piece was written to the output by the attention kernel, and
-    // so were the zero / NaN rows of empty or invalid sequences (np = 0)
-    if (np <= 1) return;
-    const int64_t prow0 = (seg + info.x) * g + hh;   // piece p: piece row prow0 + p * g
+    const int ns = max(info.y - info.x + 1, 0);   // stream pieces
+    int npre = 0;                                 // prefix pieces
+    if (a.prefix_lens != nullptr) {
+        const int b = (int)(row / a.n_q);
+        const int pl = row_prefix_len(a.context_lens[b], a.prefix_lens[b], a.max_blocks,
+                                      a.prefix_blocks);
+        npre = pl > 0 ? (pl + kPrefixChunk - 1) / kPrefixChunk : 0;
+    }
+    // without prefix pieces, a single piece was written to the output by the
+    // attention kernel, and so were the zero / NaN rows of empty or invalid
+    // sequences (no piece)
+    if (npre == 0 && ns <= 1) return;
+    const int np = ns + npre;
+    const int64_t prow0 = (seg + info.x) * g + hh;   // stream piece p: piece row prow0 + p * g
+    const int64_t rows = (int64_t)a.B * a.n_q;
+    // piece p's partial output and statistics
+    auto po = [&](int p) {
+        return p < ns ? a.part_o + (prow0 + (int64_t)p * g) * HD
+                      : a.pre_o + ((int64_t)(p - ns) * rows + row) * HD;
+    };
+    auto pm = [&](int p) {
+        return p < ns ? a.part_ml + (prow0 + (int64_t)p * g) * 2
+                      : a.pre_ml + ((int64_t)(p - ns) * rows + row) * 2;
+    };
     const int c = lane % C, h = lane / C;
     float M = -__builtin_inff(), L = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -389,11 +409,10 @@ __global__ void __launch_bounds__(kThreads) k_merge_rows(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
             const int p = h + H * k;
-            ov[k] = p < nb ? *((const f32x4*)(a.part_o + (prow0 + (int64_t)(p0 + p) * g) * HD) + c)
-                           : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            ov[k] = p < nb ? *((const f32x4*)po(p0 + p) + c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         float2 st = make_float2(0.0f, 0.0f);
-        if (lane < nb) st = *(const float2*)(a.part_ml + (prow0 + (int64_t)(p0 + lane) * g) * 2);
+        if (lane < nb) st = *(const float2*)pm(p0 + lane);
         float mb = st.y != 0.0f ? st.x : -__builtin_inff();
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) mb = fmaxf(mb, __shfl_xor(mb, o, 64));
@@ -463,8 +482,8 @@ hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s) {
     // split a row's columns over several workgroups only when segments
     // average many pieces (long sequences in a small batch)
     const bool wide = (int64_t)a.nw >= 64 * (int64_t)a.B * a.n_kv;
-    if (!wide && a.prefix_lens == nullptr && a.k_res == nullptr) {
-        // only stream pieces, few per row: one wave per row. (Rows with many
+    if (!wide && a.k_res == nullptr) {
+        // few pieces per row (stream and prefix pieces): one wave per row. (Rows with many
         // pieces keep the block-wide merge: split over column slices, waves
         // per row measured slower there, with fewer loads in flight.)
         const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64)));
