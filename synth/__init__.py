@@ -74,7 +74,8 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of the study (shapes from the pages; recipe in the design doc).
+# The five workloads of the study (shapes from the pages), and three variants of
+# the 70B layer (sliding window with sinks, 4-bit cache) defined below.
 TINY_MHA = Workload("tiny_mha", 1, B=1, n_q=4, n_kv=4, d_h=64, block_size=16,
                     kv_dtype=F32, q_dtype=F32, ctx_lo=256, ctx_hi=256, pool_blocks=32)
 LLAMA8B_LAYER = Workload("llama3_8b_layer", 2, B=32, n_q=32, n_kv=8, d_h=128, block_size=16,

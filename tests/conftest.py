@@ -9,8 +9,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# Build what is missing (the checker and the library are compiled in-tree; a
-# GPU machine receives the built files with the tree and never rebuilds here).
+# Build what is missing (the oracle and the library are compiled in-tree; a
+# machine that receives the tree with its built files does not rebuild them).
 from oracle import build as _oracle_build  # noqa: E402
 from decode_attention_paged_slot_amd import build as _pda_build  # noqa: E402
 
