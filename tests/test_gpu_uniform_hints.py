@@ -61,6 +61,45 @@ def test_uniform_rows_hint_settings(kv_dtype, d_h, g, nw, n):
     assert (_bits(unknown) == _bits(unknown_short)).all()
 
 
+@pytest.mark.parametrize("kv_dtype", [BF16, FP8])
+@pytest.mark.parametrize("nw", [7, 64, 200])
+def test_full_row_hint_that_does_not_hold(kv_dtype, nw):
+    """total_context = B * max_context claims that every row is full; here
+    the rows are ragged (an empty row, a one-token row, a row longer than
+    max_context among them). With the wave count fixed, the claim must not
+    change a bit against no hint at all. nw = 200 (>= 64 pieces per segment
+    on average) takes the column-split merge."""
+    ctx = [3000, 0, 1, 2990, 17, 3100]
+    B, n_kv = len(ctx), 1
+    c = make_case(9200 + nw + kv_dtype, ctx, n_q=4, n_kv=n_kv, d_h=128, kv_dtype=kv_dtype,
+                  max_blocks=(3100 + 15) // 16)
+    _say(f"full-row hint that does not hold kv={kv_dtype} nw={nw}")
+    claimed, _ = run_case(c, max_context=3000, total_context=B * 3000, num_partitions=nw)
+    none, _ = run_case(c, max_context=3000, total_context=0, num_partitions=nw)
+    assert (_bits(claimed) == _bits(none)).all()
+    ref = c.oracle_out()
+    keep = [0, 2, 3, 4, 5]
+    assert (claimed[1] == 0).all()
+    assert max_err(claimed[keep], ref[keep]) < (TOL_8BIT if kv_dtype == FP8 else TOL_16BIT)
+
+
+@pytest.mark.parametrize("kv_dtype", [BF16, INT8])
+@pytest.mark.parametrize("n", [16, 2000, 40000])
+def test_full_rows_column_split_merge(kv_dtype, n):
+    """Full rows split finely enough for the column-split merge (many pieces
+    per segment), with exact hints and with max_context one token short:
+    same bits, and the oracle's result."""
+    B, n_kv = 2, 2
+    nw = 64 * B * n_kv + 3
+    c = make_case(9250 + n + kv_dtype, [n] * B, n_q=8, n_kv=n_kv, d_h=128, kv_dtype=kv_dtype)
+    _say(f"full rows column-split merge kv={kv_dtype} n={n}")
+    exact, _ = run_case(c, max_context=n, total_context=B * n, num_partitions=nw)
+    short, _ = run_case(c, max_context=n - 1, total_context=B * n, num_partitions=nw)
+    assert (_bits(exact) == _bits(short)).all()
+    tol = TOL_8BIT if kv_dtype == INT8 else TOL_16BIT
+    assert max_err(exact, c.oracle_out()) < tol
+
+
 @pytest.mark.parametrize("window,sinks", [(100, 4), (33, 0), (4000, 20)])
 @pytest.mark.parametrize("nw", [0, 9])
 def test_uniform_rows_with_window(window, sinks, nw):
