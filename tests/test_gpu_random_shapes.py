@@ -1,5 +1,5 @@
 """Seeded random configurations against the oracle: the attention call,
-and the fused decode step.
+the fused decode step and the shared-prefix call.
 
 The other parity tests walk grids of one or two parameters at a time; here
 each case draws every parameter at once: head dimension, KV heads, group
@@ -159,3 +159,35 @@ def test_random_fused_step(i):
     keep = np.repeat(c.ctx > 0, c.n_q)
     assert (got[~keep] == 0).all()
     assert max_err(got[keep], ref[keep]) < (TOL_8BIT if quant else TOL_16BIT)
+
+
+N_PREFIX_CASES = 16
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_PREFIX_CASES))
+def test_random_shared_prefix(i):
+    """The shared-prefix call on random configurations: a random number of
+    shared blocks (one chunk or several, with a partial last chunk), each
+    row's prefix length drawn up to its own limit (zero included), the rows'
+    own prefix entries unmapped, against the oracle over the prefix table."""
+    from tests import test_gpu_prefix as pfx
+
+    d = _draw(2000 + i)
+    r = np.random.default_rng(81_000 + i)
+    kv_dtype = (BF16, FP8, INT8)[i % 3]
+    n_shared = int(r.integers(1, 60))
+    ctx = [max(n, 1) for n in d["ctx"]]
+    ctx[0] = max(ctx[0], 16 * n_shared + 1)          # one row can hold the whole prefix
+    print(f"random shared prefix {i}: kv={kv_dtype} shared={n_shared} {d}", flush=True)
+    sys.stdout.flush()
+    c = make_case(82_000 + i, ctx, n_q=d["g"] * d["n_kv"], n_kv=d["n_kv"], d_h=d["d_h"],
+                  kv_dtype=kv_dtype, q_dtype=d["q_dtype"], shared_prefix_blocks=n_shared)
+    top = pfx._prefix_lens(c, n_shared)
+    pl = np.array([int(r.integers(0, t + 1)) for t in top], dtype=np.int32)
+    pl[0] = top[0]
+    got, _, _ = pfx._run(c, c.shared_ids, pl, nw=d["nw"])
+    ref, invalid, bad = pfx._oracle(c, c.shared_ids, pl)
+    assert bad == 0 and not invalid.any()
+    tol = TOL_8BIT if kv_dtype in (FP8, INT8) else TOL_16BIT
+    assert max_err(got, ref) < tol
