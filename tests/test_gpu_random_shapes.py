@@ -1,5 +1,5 @@
 """Seeded random configurations against the oracle: the attention call,
-the fused decode step and the shared-prefix call.
+the fused decode step, the shared-prefix call and the 4-bit call.
 
 The other parity tests walk grids of one or two parameters at a time; here
 each case draws every parameter at once: head dimension, KV heads, group
@@ -191,3 +191,40 @@ def test_random_shared_prefix(i):
     assert bad == 0 and not invalid.any()
     tol = TOL_8BIT if kv_dtype in (FP8, INT8) else TOL_16BIT
     assert max_err(got, ref) < tol
+
+
+N_INT4_CASES = 12
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_INT4_CASES))
+def test_random_int4_attention(i):
+    """4-bit attention (encoded blocks plus each row's residual window) on
+    random configurations, with NaN-poisoned blocks and residual slots that
+    must not be read, against the oracle."""
+    import oracle
+    import synth
+    from tests import test_gpu_int4 as i4
+    from tests.gpu_helpers import to_dev
+
+    d = _draw(3000 + i)
+    print(f"random 4-bit {i}: {d}", flush=True)
+    sys.stdout.flush()
+    n_q = d["g"] * d["n_kv"]
+    st, ks, table, ctx, nb, mb = i4._case(83_000 + i, d["ctx"], n_q=n_q, n_kv=d["n_kv"],
+                                          d_h=d["d_h"])
+    r = np.random.default_rng(84_000 + i)
+    q_np = synth.gaussian((ctx.size, n_q, d["d_h"]), d["q_dtype"], r)
+    st_d, ks_d = i4._dev(st, ks, "cuda")
+    q = to_dev(q_np, d["q_dtype"], "cuda")
+    scale = 1.0 / np.sqrt(d["d_h"])
+    got = i4._attend(st_d, ks_d, q, table, ctx, scale,
+                     i4._desc(ctx.size, n_q, d["n_kv"], d["d_h"], mb, nb, d["q_dtype"], F32,
+                              ctx, d["nw"]))
+    ref, _, _, bad = oracle.paged_attn_int4(q_np, st, ks, table, ctx, scale, n_q=n_q,
+                                            n_kv=d["n_kv"], q_dtype=d["q_dtype"])
+    assert bad == 0
+    ref = ref.reshape(got.shape)
+    empty = ctx == 0
+    assert (got[empty] == 0).all()
+    assert max_err(got[~empty], ref[~empty]) < TOL_8BIT
