@@ -257,7 +257,19 @@ int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
  * for any such row before launching. It checks the blocks the call looks up,
  * as the kernels do: blocks a sliding window skips are not looked up (nor,
  * in the _prefix calls, a row's own entries below its prefix length, nor, in
- * the _int4 calls, a row's open block). */
+ * the _int4 calls, a row's open block).
+ * Tuning overrides, read from the environment at each call and by
+ * pda_attn_workspace_size, so keep them fixed between the two (defaults are
+ * the measured best on MI355X; any value gives a correct result, only the
+ * split, and with it the rounding order, changes):
+ *   PDA_ATTN_WORKGROUPS      workgroups of the split (4 wave ranges each);
+ *                            default 256 for 16-bit caches, 512 for 8-bit
+ *                            and 4-bit ones
+ *   PDA_MIN_BLOCKS_PER_WAVE  fewest expected blocks per wave range before the
+ *                            split shrinks the wave count (default 8)
+ *   PDA_SEGMENT_COST         extra units charged per (sequence, KV head)
+ *                            segment when ranges are cut (default 0; 4 for
+ *                            the _prefix calls) */
 int32_t pda_paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* context_lens, float scale,
                               void* out, const pda_attn_desc* d, void* workspace,
