@@ -219,7 +219,10 @@ typedef struct pda_attn_desc {
  * call runs unsplit and without a shared prefix). The workspace holds the
  * split-KV partial results (normalised output, max, sum per piece) and the
  * split bookkeeping; its layout is internal to the library and nothing in
- * it needs clearing between calls. Host-only. */
+ * it needs clearing between calls. A call writes the workspace and then
+ * reads it back in a later kernel on the same stream, so two calls that may
+ * run at the same time (on different streams) need separate workspaces;
+ * calls ordered on one stream can share one. Host-only. */
 int32_t pda_attn_workspace_size(const pda_attn_desc* d, size_t* bytes);
 
 /* The split chosen for this descriptor: *num_partitions = P (1 = unsplit) and
