@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI: argument validation, split planning and dispatch.
 // Every device call is one or two kernel launches on the caller's stream.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -85,9 +86,11 @@ Plan make_stream_plan_split(const pda_attn_desc& d, int64_t S, int64_t t_est);
 // Stream plan (16-bit and 8-bit caches). Measured on MI355X: the step runs
 // at its best when every compute unit holds the same amount of work, and one
 // workgroup of four streaming waves per compute unit already saturates HBM
-// with a bf16 cache; so the default is 256 workgroups (1024 wave ranges) for
-// bf16 and 512 for 8-bit caches, fewer when the batch has under 8 blocks per
-// range. The block count T is estimated from the
+// with a bf16 cache; so the default is one workgroup per compute unit of the
+// current device (256 on an MI355X: 1024 wave ranges) for bf16 and two for
+// 8-bit caches, fewer when the batch has under 8 blocks per range. One more
+// workgroup than the device runs at once costs ~60% (the equal ranges then
+// wait on a second round). The block count T is estimated from the
 // host hints (total_context, else B * max_context); the kernel recomputes the
 // exact split from context_lens, so the estimate only tunes the wave count.
 Plan make_stream_plan(const pda_attn_desc& d) {
@@ -115,6 +118,33 @@ Plan make_stream_plan(const pda_attn_desc& d) {
     return make_stream_plan_split(d, S, t_est);
 }
 
+// Compute units of the current device, cached per device ordinal; 256 (an
+// MI355X, one partition) when no device is current or the query fails. The
+// streaming kernel's equal wave ranges assume that all of its workgroups run
+// at once, so the default workgroup count follows the device's CU count
+// (a partitioned GPU exposes fewer CUs per device).
+int64_t device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // The split part of the stream plan (see make_stream_plan).
 Plan make_stream_plan_split(const pda_attn_desc& d, int64_t S, int64_t t_est) {
     const int64_t nblk_max = std::min<int64_t>(
@@ -124,11 +154,14 @@ Plan make_stream_plan_split(const pda_attn_desc& d, int64_t S, int64_t t_est) {
     if (d.num_partitions > 1) {
         nw = d.num_partitions;
     } else {
-        // 8-bit caches do twice the conversion and matrix work per byte and
-        // need two workgroups per compute unit to keep HBM busy
+        // one workgroup per compute unit; 8-bit caches do twice the
+        // conversion and matrix work per byte and need two per compute unit
+        // to keep HBM busy
         const bool eight_bit = d.kv_dtype == PDA_FP8_E4M3 || d.kv_dtype == PDA_INT8 ||
                                d.kv_dtype == PDA_INT4;
-        const int64_t wgs = std::max(env_int("PDA_ATTN_WORKGROUPS", eight_bit ? 512 : 256), 1);
+        const int64_t cus = device_cus();
+        const int64_t wgs = std::max<int64_t>(
+            env_int("PDA_ATTN_WORKGROUPS", (int)(eight_bit ? 2 * cus : cus)), 1);
         const int64_t min_blocks = std::max(env_int("PDA_MIN_BLOCKS_PER_WAVE", 8), 1);
         nw = std::min<int64_t>(4 * wgs, (t_est + min_blocks - 1) / min_blocks);
         // short contexts (a few blocks per segment): one wave per segment, no merge

@@ -266,8 +266,9 @@ int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
  * the measured best on MI355X; any value gives a correct result, only the
  * split, and with it the rounding order, changes):
  *   PDA_ATTN_WORKGROUPS      workgroups of the split (4 wave ranges each);
- *                            default 256 for 16-bit caches, 512 for 8-bit
- *                            and 4-bit ones
+ *                            default one per compute unit of the current
+ *                            device (256 on an MI355X) for 16-bit caches,
+ *                            two per compute unit for 8-bit and 4-bit ones
  *   PDA_MIN_BLOCKS_PER_WAVE  fewest expected blocks per wave range before the
  *                            split shrinks the wave count (default 8)
  *   PDA_SEGMENT_COST         extra units charged per (sequence, KV head)
