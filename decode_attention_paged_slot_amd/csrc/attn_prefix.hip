@@ -17,8 +17,9 @@
 // Work decomposition. A workgroup takes (KV head, chunk, query group of 64
 // queries); query qi = b * g + hh of head group j is output row
 // b * n_q + j * g + hh. It issues its query loads, reads the chunk's block
-// ids and scales into LDS, then issues the loads of all of the chunk's K and
-// V tiles at once (one memory round trip) and writes them to LDS as bf16
+// ids into LDS, then issues the loads of all of the chunk's K and V tiles
+// and of the blocks' scales at once (one memory round trip) and writes them
+// to LDS, the tiles as bf16
 // (8-bit caches are converted here, once per workgroup). Eight waves share
 // the tiles: wave w owns the 16 queries of tile w % 4 (the N columns of its
 // matrix products) over the chunk's blocks of parity w / 4, two blocks per
@@ -131,17 +132,15 @@ __global__ void __launch_bounds__(kPrefixThreads) k_attn_prefix(AttnArgs a, int3
     for (int m = 32; m >= 1; m >>= 1) wn = max(wn, __shfl_xor(wn, m, 64));
     wn = __builtin_amdgcn_readfirstlane(wn);
     if (lane == 0) wneed[wave] = wn;
-    // the chunk's block ids and scales (one lane per block); an unmapped
-    // entry is read as block 0 and its tiles zeroed, its rows poisoned below
+    // the chunk's block ids (one lane per block); an unmapped entry is read
+    // as block 0 and its tiles zeroed, its rows poisoned below
+    int sid = -1;   // this lane's block id, for its block's scales
     if ((int)threadIdx.x < kPrefixChunk) {
         const int blk = threadIdx.x;
         int id = blk < a.prefix_blocks - i0 ? a.prefix_table[i0 + blk] : 0;
         const bool ok = id >= 0 && id < a.num_blocks;
         idl[blk] = ok ? id : -1;
-        if (QUANT) {
-            ksl[blk] = ok ? a.k_scale[(int64_t)id * n_kv + j] : 0.0f;
-            vsl[blk] = ok ? a.v_scale[(int64_t)id * n_kv + j] : 0.0f;
-        }
+        sid = ok ? id : -1;
     }
     __syncthreads();
     int nb = 0;
@@ -161,6 +160,16 @@ __global__ void __launch_bounds__(kPrefixThreads) k_attn_prefix(AttnArgs a, int3
         const char* base = (ch < HALF ? (const char*)a.k : (const char*)a.v) +
                            (int64_t)id * block_stride + head_off + 16 * (ch % HALF);
         raw[l] = *(const uint4*)base;
+    }
+    // the block scales, requested after the tiles so that the two share a
+    // round trip (the loop reads them after the barrier below)
+    if constexpr (QUANT) {
+        if ((int)threadIdx.x < kPrefixChunk) {
+            ksl[threadIdx.x] = sid >= 0 ? a.k_scale[(int64_t)sid * n_kv + j] : 0.0f;
+            vsl[threadIdx.x] = sid >= 0 ? a.v_scale[(int64_t)sid * n_kv + j] : 0.0f;
+        }
+    } else {
+        (void)sid;
     }
     // to LDS as bf16: K rows with the chunk XOR swizzle of the operand read,
     // V rows in the layout of the transposed reads
