@@ -100,6 +100,26 @@ def test_workspace_and_plan():
     assert pda.attn_workspace_size(d) >= 2 * 8 * 4 * (128 + 2) * 4
 
 
+def test_workgroup_override(monkeypatch):
+    # the environment override is read at each call, by the size query and
+    # the plan alike; without a device the default assumes 256 compute units
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count \
+        if torch.cuda.is_available() else 256
+    d = _desc(B=8, n_q=64, n_kv=8, max_blocks_per_seq=2048, num_blocks=18205,
+              max_context=32768, total_context=8 * 32768)
+    assert pda.attn_plan(d)[0] == 4 * cus
+    q = _desc(B=8, n_q=64, n_kv=8, max_blocks_per_seq=2048, num_blocks=18205,
+              max_context=32768, total_context=8 * 32768, kv_dtype=pda.FP8_E4M3)
+    assert pda.attn_plan(q)[0] == 8 * cus
+    ws_default = pda.attn_workspace_size(d)
+    monkeypatch.setenv("PDA_ATTN_WORKGROUPS", "100")
+    assert pda.attn_plan(d)[0] == 400 and pda.attn_plan(q)[0] == 400
+    assert pda.attn_workspace_size(d) < ws_default
+    monkeypatch.delenv("PDA_ATTN_WORKGROUPS")
+    assert pda.attn_plan(d)[0] == 4 * cus
+
+
 def test_stream_plan_limits():
     # more than 4096 sequences, or a flattened block axis of 2^31, in one call
     with pytest.raises(pda.PdaError):

@@ -62,3 +62,18 @@ def test_widest_group_most_waves(kv_dtype):
     got, _ = run_case(c, num_partitions=MAX_WAVES)
     tol = TOL_8BIT if kv_dtype == FP8 else TOL_16BIT
     assert max_err(got, c.oracle_out()) < tol
+
+
+def test_default_split_follows_the_device():
+    """With a device current, the default plan takes one workgroup (four
+    wave ranges) per compute unit for a 16-bit cache and two for an 8-bit
+    one, when the work is large enough."""
+    import torch
+    import decode_attention_paged_slot_amd as pda
+    torch.cuda.init()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _say(f"default split on {cus} compute units")
+    for kv, per_cu in ((BF16, 4), (FP8, 8)):
+        d = pda.AttnDesc(8, 64, 8, 128, 16, 2048, 18205, kv, BF16, 0, 32768, 0, 8 * 32768, 0, 0,
+                         0, BF16)
+        assert pda.attn_plan(d)[0] == per_cu * cus
