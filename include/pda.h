@@ -12,9 +12,9 @@
  *    section 9.4].
  *  - Paged allocation: fixed-size blocks, a per-request block table maps
  *    logical blocks to physical blocks; a logical position resolves to
- *    (table[pos / bs], pos % bs) before the kernel reads KV memory; paging
- *    changes allocation and lookup, not the attention formula  [section 9.5,
- *    including the worked example "PagedAttention block lookup"].
+ *    (table[pos / bs], pos % bs) before the kernel reads KV memory; the
+ *    attention arithmetic itself is unchanged by paging  [section 9.5,
+ *    including its block-lookup example].
  *  - Grouped-query attention: g = n_q / n_kv query heads address one stored
  *    KV head  [GQA teaser on the kv-cache tag page; SoK paper section 1.1].
  *  - A quantized cache stores fewer bits per element plus scale metadata and

@@ -9,17 +9,18 @@ module), which hold none of the method's arithmetic.
 Contents, each written from the pages' statement of the method:
 
 * `paged_attn`      -- decode attention through a block table, fp64, two-pass
-                       softmax (C, `pda_oracle.c`). Paging changes only cache
-                       allocation and lookup, not the attention formula ("9
-                       Decode and KV Cache", section 9.5); GQA maps query head
+                       softmax (C, `pda_oracle.c`). Paging only decides where
+                       each position's rows are stored and how they are found;
+                       the arithmetic is plain attention ("9 Decode and KV
+                       Cache", section 9.5); GQA maps query head
                        h to KV head h // g (kv-cache tag page, GQA teaser; SoK
                        paper section 1.1). Optional sliding window with
                        attention sinks (section 9.7; sink and sliding-window
                        teasers on the tag page).
-* `physical_location`, `slot_of` -- the logical position -> (physical block,
-                       offset) translation of the worked example "PagedAttention
-                       block lookup" (section 9.5), and the flat slot index
-                       pb * bs + off used to address a cache row.
+* `locate`, `slot_of` -- logical position -> (physical block, offset), the
+                       translation that section 9.5's block-lookup example
+                       performs, and the flat slot index pb * bs + off used to
+                       address a cache row.
 * `kv_append`       -- the append path (section 9.4, "Append path"): each new
                        token's K/V row lands in its mapped slot, bit for bit.
 * `fp8_decode`, `quantize_fp8`, `quantize_int8`, `kv_append_quant` -- an
@@ -220,22 +221,27 @@ def prefix_block_table(block_table, context_lens, prefix_table, prefix_lens):
 
 
 # ---------------------------------------------------------- lookup and append
-def physical_location(block_table: dict, token_index: int, block_size: int = 16):
-    """Logical token position -> (physical block, offset): integer division
-    picks the logical block, the remainder is the offset inside it, and the
-    table maps the logical block to its physical block. An unmapped logical
-    block raises KeyError, as the worked example's dictionary lookup does."""
-    logical_block = token_index // block_size
-    offset = token_index % block_size
-    return block_table[logical_block], offset
+def locate(table, pos: int, block_size: int = 16):
+    """(physical block, offset in it) of logical position `pos`.
+
+    `table` maps logical block numbers to physical ones: a dict, or a
+    sequence indexed by logical block in which a negative entry means
+    "unmapped". divmod splits the position into its logical block and the
+    offset; a logical block the table does not map raises KeyError (a row
+    cannot be read there)."""
+    lb, off = divmod(int(pos), int(block_size))
+    if isinstance(table, dict):
+        pb = table.get(lb, -1)
+    else:
+        pb = int(table[lb]) if 0 <= lb < len(table) else -1
+    if pb < 0:
+        raise KeyError(lb)
+    return int(pb), off
 
 
 def slot_of(block_table_row: Sequence[int], token_index: int, block_size: int) -> int:
     """Flat cache-row index of a logical position: physical block * bs + offset."""
-    pb, off = physical_location(dict(enumerate(int(x) for x in block_table_row)),
-                                token_index, block_size)
-    if pb < 0:
-        raise KeyError(token_index // block_size)
+    pb, off = locate(block_table_row, token_index, block_size)
     return pb * block_size + off
 
 

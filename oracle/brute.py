@@ -3,8 +3,9 @@
 A second, structurally different route to the same definition as the C
 oracle: first walk every logical position through the block table to gather a
 contiguous K and V per sequence, then apply softmax(q K^T * scale) V with
-matrix products. Paging changes cache allocation and lookup, not the attention
-formula ("9 Decode and KV Cache", section 9.5), so the two must agree.
+matrix products. Paging only decides where each position's rows are stored
+and how they are found, so the result must equal plain attention over the
+gathered rows ("9 Decode and KV Cache", section 9.5): the two must agree.
 Intended for tiny inputs only.
 """
 from __future__ import annotations

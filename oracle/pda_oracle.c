@@ -7,9 +7,10 @@
  * GPU library: every decode, lookup and reduction below is written out here
  * from the definitions.
  *
- * What it computes (the plain definition, since block paging changes only
- * where a token's key/value live, not the attention formula -- "9 Decode and
- * KV Cache", section 9.5, PagedAttention):
+ * What it computes (the plain definition: block paging only moves where a
+ * token's key/value rows are stored and how they are found, the arithmetic
+ * is ordinary attention -- "9 Decode and KV Cache", section 9.5,
+ * PagedAttention):
  *
  *   for each sequence b and query head h, with g = n_q / n_kv and the KV head
  *   j = h / g (grouped-query attention: several query heads read one stored

@@ -44,10 +44,10 @@ def test_block_lookup_worked_example():
     g = json.load(open(os.path.join(GOLDEN, "block_lookup.json")))
     table = {int(k): v for k, v in g["block_table"].items()}
     for tok, pb, off in g["cases"]:
-        assert oracle.physical_location(table, tok, g["block_size"]) == (pb, off)
+        assert oracle.locate(table, tok, g["block_size"]) == (pb, off)
     for tok in g["unmapped_tokens"]:
         with pytest.raises(KeyError):
-            oracle.physical_location(table, tok, g["block_size"])
+            oracle.locate(table, tok, g["block_size"])
     row = [table[i] for i in range(3)] + [-1]
     for tok, pb, off in g["cases"]:
         assert oracle.slot_of(row, tok, g["block_size"]) == pb * g["block_size"] + off
