@@ -713,4 +713,27 @@ int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, i
     return e == hipSuccess ? PDA_OK : hip_fail("merge launch", e);
 }
 
+int32_t pda_hbm_read_probe(const void* buf, size_t bytes, const int64_t* tile_offsets,
+                           int64_t n_tiles, int32_t tile_bytes, int32_t waves, uint32_t* sink,
+                           void* stream) {
+    if (!buf || !sink || !aligned16(buf) || waves < 4 || waves > 65536 || waves % 4 != 0) {
+        set_error("read probe: buf and sink non-NULL, buf 16-byte aligned, waves a multiple "
+                  "of 4 in [4, 65536]");
+        return PDA_EINVAL;
+    }
+    if (tile_offsets == nullptr) {
+        if (bytes / 4096 < (size_t)waves) {
+            set_error("read probe: %zu bytes is less than one 4 KiB step per wave", bytes);
+            return PDA_EINVAL;
+        }
+    } else if (n_tiles < 0 || (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 &&
+                               tile_bytes != 8192) || (size_t)tile_bytes > bytes) {
+        set_error("read probe: n_tiles >= 0 and tile_bytes 1024, 2048, 4096 or 8192");
+        return PDA_EINVAL;
+    }
+    hipError_t e = launch_read_probe(buf, bytes, tile_offsets, n_tiles, tile_bytes, waves, sink,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? PDA_OK : hip_fail("read probe launch", e);
+}
+
 }  // extern "C"

@@ -429,6 +429,32 @@ int32_t pda_paged_decode_attn_int4(const void* q, const void* k_q, const void* v
 int32_t pda_lse_merge(const float* part_o, const float* part_ml, int32_t rows, int32_t P,
                       int32_t d_h, float* out, void* stream);
 
+/* ------------------------------------------------------ measurement probe
+ * Read-only HBM probe: the bandwidth plain loads reach on this device, the
+ * practical ceiling beside the vendor peak for a path that is bound by
+ * reading the cache ("9 Decode and KV Cache", section 9.8: bytes moved over
+ * elapsed time against the sustained bandwidth). Not part of the method.
+ *   buf           device, 16-byte aligned, `bytes` long (read only).
+ *   tile_offsets  NULL: sequential mode. `waves` waves walk buf in 4 KiB
+ *                 steps, wave w reading bytes [(s * waves + w) * 4096, +4096)
+ *                 of step s, for floor(bytes / 4096 / waves) steps.
+ *                 Otherwise device int64 [n_tiles]: tile mode. Tile i is the
+ *                 `tile_bytes` bytes at buf + tile_offsets[i]; wave w reads
+ *                 tiles [w * n_tiles / waves, (w + 1) * n_tiles / waves) in
+ *                 order with four tiles in flight. The caller guarantees that
+ *                 every offset is a multiple of 16 and offset + tile_bytes <=
+ *                 bytes (device data is not inspected).
+ *   tile_bytes    1024, 2048, 4096 or 8192 (tile mode).
+ *   waves         multiple of 4 in [4, 65536]: 64-lane waves, four per
+ *                 workgroup.
+ *   sink          device uint32 [waves * 64]: a checksum of every dword read
+ *                 (so no load is elided), overwritten.
+ * Loads are 16 bytes per lane and non-temporal, like the attention
+ * kernels' cache loads. EINVAL on a NULL buffer, bad sizes or alignment. */
+int32_t pda_hbm_read_probe(const void* buf, size_t bytes, const int64_t* tile_offsets,
+                           int64_t n_tiles, int32_t tile_bytes, int32_t waves, uint32_t* sink,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif
