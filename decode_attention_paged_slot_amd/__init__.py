@@ -21,6 +21,7 @@ _BINDING_NAMES = (
     "paged_decode_attn", "paged_decode_attn_quant", "lse_merge",
     "decode_step", "decode_step_quant", "paged_decode_attn_prefix", "decode_step_prefix",
     "kv_append_int4", "paged_decode_attn_int4", "hbm_read_probe", "BoundCall",
+    "paged_decode_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
 )
 
 __all__ = list(_BINDING_NAMES)

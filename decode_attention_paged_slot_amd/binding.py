@@ -104,7 +104,10 @@ _SIGS = {
                                           ctypes.c_float, _vp, ctypes.POINTER(AttnDesc), _vp,
                                           _sz, _vp]),
     "pda_hbm_read_probe": (_i32, [_vp, _sz, _vp, _i64, _i32, _i32, _vp, _vp]),
+    "pda_paged_decode_attn_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                             ctypes.POINTER(AttnDesc), _vp]),
 }
+NOALLOC_SCRATCH_BYTES = 16 << 20   # PDA_NOALLOC_SCRATCH_BYTES
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
     _f.restype = _res
@@ -314,8 +317,8 @@ def attn_plan(desc: AttnDesc):
 
 
 def workspace_for(desc: AttnDesc, device):
-    """A zero-filled workspace tensor of the size the descriptor needs (or
-    None). The library requires zeros on first use and leaves them behind."""
+    """A workspace tensor of the size the descriptor needs (or None),
+    zero-filled so that its contents are the same on every run."""
     n = attn_workspace_size(desc)
     if n == 0:
         return None
@@ -374,6 +377,25 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, context_lens, scale: flo
                    (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
                     float(scale), _ptr(out), desc, _ptr(workspace), ws_bytes, _stream(stream)),
                    (q, k_cache, v_cache, block_table, context_lens, out, workspace), bind)
+
+
+def paged_decode_attn_noalloc(q, k_cache, v_cache, block_table, context_lens, scale: float,
+                              out, *, desc: Optional[AttnDesc] = None, max_context: int = 0,
+                              num_partitions: int = 0, total_context: int = 0,
+                              reuse_prefix_blocks: int = 0, window: int = 0, sink_tokens: int = 0,
+                              stream=None, bind=False):
+    """pda_paged_decode_attn_noalloc: as paged_decode_attn, with the workspace
+    taken from the library's fixed device scratch (no allocation anywhere)."""
+    if desc is None:
+        desc = attn_desc(q, k_cache, block_table, max_context=max_context,
+                         out_dtype=dtype_code(out), num_partitions=num_partitions,
+                         total_context=total_context, reuse_prefix_blocks=reuse_prefix_blocks,
+                         window=window, sink_tokens=sink_tokens)
+    _check_attn(desc, q, k_cache, v_cache, block_table, context_lens, out)
+    return _launch("pda_paged_decode_attn_noalloc",
+                   (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
+                    float(scale), _ptr(out), desc, _stream(stream)),
+                   (q, k_cache, v_cache, block_table, context_lens, out), bind)
 
 
 def paged_decode_attn_quant(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,

@@ -279,6 +279,27 @@ int32_t pda_paged_decode_attn(const void* q, const void* k_cache, const void* v_
                               void* out, const pda_attn_desc* d, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as pda_paged_decode_attn, with the workspace taken from a fixed
+ * device array of the library instead of the caller. Nothing is allocated:
+ * no hipMalloc, hipFree or allocating library routine is called. The array
+ * holds PDA_NOALLOC_SCRATCH_BYTES bytes on every device the library runs
+ * on, kept until the process ends; its device address is looked up once per
+ * device, on the first call with that device current. A descriptor whose
+ * pda_attn_workspace_size exceeds the limit returns PDA_EWORKSPACE (use
+ * pda_paged_decode_attn with a caller workspace then). The array needs no
+ * clearing between calls. All calls on one device share its array, so two
+ * such calls whose kernels may overlap (different streams of one device)
+ * race and corrupt each other's results; order them on one stream.
+ * Arguments, row semantics and other errors as for pda_paged_decode_attn
+ * (f32 and bf16 caches). */
+#define PDA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t pda_paged_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* context_lens,
+                                      float scale, void* out, const pda_attn_desc* d,
+                                      void* stream);
+
 /* Quantized-cache variant: kv_dtype PDA_FP8_E4M3 or PDA_INT8 and
  *   K = k_scale[pb][j] * dec(K_code),  V = v_scale[pb][j] * dec(V_code)
  * with k_scale, v_scale device [num_blocks][n_kv] fp32. The scales are folded
