@@ -6,7 +6,22 @@ import numpy as np
 from synth import F32, BF16, FP8, INT8
 
 TOL_16BIT = 5e-3     # bf16 / fp32 caches: max-abs error vs the fp64 oracle
-TOL_8BIT = 3e-2      # fp8 / int8 caches: vs the oracle on the dequantized cache
+TOL_8BIT = 3e-2      # fp8 / int8 / 4-bit caches: vs the oracle on the dequantized cache
+# Regression bound beside the contract bars: the kernels keep ~16 bits of
+# every weight and fp32 query (bf16 hi + lo parts) and accumulate in fp32, so
+# they reach 1e-7 .. 1e-5 of the oracle on every cache type; a lost precision
+# step (a dropped lo part, a bf16-only scaled query) lands far above 1e-4
+# while still inside the bars.
+TOL_REGRESSION = 1e-4
+
+
+def assert_parity(err: float, bar: float, regression=TOL_REGRESSION) -> None:
+    """max-abs error within the contract bar and within the regression bound
+    (regression=None where the output itself is rounded, e.g. bf16 out)."""
+    assert err < bar, f"max-abs error {err:.3g} over the contract bar {bar}"
+    if regression is not None:
+        assert err < regression, (f"max-abs error {err:.3g} over the regression bound "
+                                  f"{regression} (contract bar {bar})")
 
 
 def torch_dtype(code: int):

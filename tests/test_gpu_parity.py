@@ -2,12 +2,14 @@
 
 Small cases (many tiles, ragged tails, every dtype and head-group size) are
 compared element by element. Bars: max-abs 5e-3 for bf16 / fp32 caches, 3e-2
-for fp8 / int8 caches against the oracle on the dequantized cache; bit-exact
+for fp8 / int8 caches against the oracle on the dequantized cache, and beside
+them a 1e-4 regression bound on the precision the kernels reach; bit-exact
 for appends and for invariances that fix the reduction order (physical block
 renumbering, prefix aliasing, reruns).
 """
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -16,7 +18,7 @@ import pytest
 import oracle
 from synth import F32, BF16, FP8, INT8
 from tests.helpers import make_case, permute_physical, unshare
-from tests.gpu_helpers import TOL_16BIT, TOL_8BIT, max_err, run_case, to_dev
+from tests.gpu_helpers import TOL_16BIT, TOL_8BIT, TOL_REGRESSION, assert_parity, max_err, run_case, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +39,7 @@ def test_bf16_cache_ragged(d_h, g):
     _say(f"bf16 cache d_h={d_h} g={g}")
     got, _ = run_case(c)
     ref = c.oracle_out()
-    assert max_err(got, ref) < TOL_16BIT
+    assert_parity(max_err(got, ref), TOL_16BIT)
 
 
 @pytest.mark.parametrize("parts", [1, 2, 3, 7, 0])
@@ -46,7 +48,7 @@ def test_split_partitions_agree(parts):
     _say(f"split partitions={parts}")
     got, desc = run_case(c, num_partitions=parts)
     ref = c.oracle_out()
-    assert max_err(got, ref) < TOL_16BIT
+    assert_parity(max_err(got, ref), TOL_16BIT)
 
 
 @pytest.mark.parametrize("nw", [2, 3, 5, 7, 13, 64, 1000])
@@ -63,7 +65,7 @@ def test_stream_ranges_ragged_with_empty_rows(nw, kv_dtype):
     ref = c.oracle_out()
     for b in (0, 3, 7):
         assert (got[b] == 0).all()
-    assert max_err(got, ref) < (TOL_8BIT if kv_dtype == FP8 else TOL_16BIT)
+    assert_parity(max_err(got, ref), (TOL_8BIT if kv_dtype == FP8 else TOL_16BIT))
 
 
 @pytest.mark.parametrize("d_h", [64, 128])
@@ -76,9 +78,9 @@ def test_stream_default_plan_many_short_rows(d_h, g):
     c = make_case(2600 + d_h + g, ctx, n_q=g * n_kv, n_kv=n_kv, d_h=d_h)
     _say(f"stream default plan d_h={d_h} g={g}")
     got, _ = run_case(c, total_context=int(sum(ctx)))
-    assert max_err(got, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got, c.oracle_out()), TOL_16BIT)
     got2, _ = run_case(c, num_partitions=97)
-    assert max_err(got2, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got2, c.oracle_out()), TOL_16BIT)
 
 
 WINDOWS = [(1, 0), (20, 4), (33, 17), (100, 0), (5, 40), (4096, 4)]
@@ -111,14 +113,14 @@ def test_window_with_sinks(kv_dtype, window, sinks, nw):
     got, _ = run_case(c, table=table, window=window, sinks=sinks, num_partitions=nw)
     ref = c.oracle_out(window=window, sinks=sinks)
     assert (got[0] == 0).all()
-    assert max_err(got, ref) < (TOL_8BIT if kv_dtype == FP8 else TOL_16BIT)
+    assert_parity(max_err(got, ref), (TOL_8BIT if kv_dtype == FP8 else TOL_16BIT))
 
 
 def test_fp32_query_with_bf16_cache():
     c = make_case(3001, CTX_RAGGED, n_q=8, n_kv=2, d_h=128, q_dtype=F32)
     _say("fp32 q, bf16 cache")
     got, _ = run_case(c)
-    assert max_err(got, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got, c.oracle_out()), TOL_16BIT)
 
 
 @pytest.mark.parametrize("q_dtype", [F32, BF16])
@@ -128,9 +130,9 @@ def test_fp32_cache(q_dtype, d_h):
                   q_dtype=q_dtype)
     _say(f"fp32 cache q={q_dtype} d_h={d_h}")
     got, _ = run_case(c)
-    assert max_err(got, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got, c.oracle_out()), TOL_16BIT)
     got2, _ = run_case(c, num_partitions=3)
-    assert max_err(got2, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got2, c.oracle_out()), TOL_16BIT)
 
 
 @pytest.mark.parametrize("kv_dtype", [FP8, INT8])
@@ -141,7 +143,7 @@ def test_quantized_cache(kv_dtype, d_h, g):
                   kv_dtype=kv_dtype)
     _say(f"quantized cache dtype={kv_dtype} d_h={d_h} g={g}")
     got, _ = run_case(c)
-    assert max_err(got, c.oracle_out()) < TOL_8BIT
+    assert_parity(max_err(got, c.oracle_out()), TOL_8BIT)
 
 
 def test_bf16_output_is_rne_of_fp32_output():
@@ -171,7 +173,7 @@ def test_prefix_aliasing_bit_identical():
     a, _ = run_case(c)
     b, _ = run_case(unshare(c))
     assert (a == b).all()
-    assert max_err(a, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(a, c.oracle_out()), TOL_16BIT)
 
 
 @pytest.mark.parametrize("kv_dtype", [BF16, FP8])
@@ -206,7 +208,7 @@ def test_empty_rows_and_single_token():
         pb = c.table[1, 0]
         for h in range(c.n_q):
             assert (got[1, h] == v[pb, h // c.g, 0, :].astype(np.float32)).all()
-        assert max_err(got[3], c.oracle_out()[3]) < TOL_16BIT
+        assert_parity(max_err(got[3], c.oracle_out()[3]), TOL_16BIT)
 
 
 @pytest.mark.parametrize("parts", [1, 3])
@@ -220,10 +222,10 @@ def test_unmapped_block_poisons_only_its_row(parts):
     got, _ = run_case(c, table=t, num_partitions=parts)
     ref = c.oracle_out()
     assert np.isnan(got[1]).all()
-    assert max_err(got[[0, 2]], ref[[0, 2]]) < TOL_16BIT
+    assert_parity(max_err(got[[0, 2]], ref[[0, 2]]), TOL_16BIT)
     got, _ = run_case(c, table=t2, num_partitions=parts)
     assert np.isnan(got[2]).all()
-    assert max_err(got[[0, 1]], ref[[0, 1]]) < TOL_16BIT
+    assert_parity(max_err(got[[0, 1]], ref[[0, 1]]), TOL_16BIT)
 
 
 @pytest.mark.parametrize("parts", [0, 1, 4])
@@ -236,7 +238,7 @@ def test_context_beyond_table_is_nan(parts):
     _say(f"context beyond table parts={parts}")
     got, _ = run_case(c2, max_context=40, num_partitions=parts)
     assert np.isnan(got[1]).all()
-    assert max_err(got[0], c.oracle_out()[0]) < TOL_16BIT
+    assert_parity(max_err(got[0], c.oracle_out()[0]), TOL_16BIT)
 
 
 def test_context_above_max_context_still_complete():
@@ -244,7 +246,7 @@ def test_context_above_max_context_still_complete():
     c = make_case(7301, [900, 50], n_q=8, n_kv=2, d_h=128)
     _say("context above max_context")
     got, _ = run_case(c, max_context=64, num_partitions=4)
-    assert max_err(got, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got, c.oracle_out()), TOL_16BIT)
 
 
 # ------------------------------------------------------------------- append
@@ -387,7 +389,7 @@ def test_merge_many_pieces_per_row(d_h, out_dtype):
     got, _ = run_case(c, num_partitions=1000, out_dtype=out_dtype)
     ref = c.oracle_out()
     tol = TOL_16BIT if out_dtype == F32 else 2e-2   # bf16 output: half an ulp at |x| < 4
-    assert max_err(got, ref) < tol
+    assert_parity(max_err(got, ref), tol, None if out_dtype == BF16 else TOL_REGRESSION)
 
 
 @pytest.mark.parametrize("d_h", [64, 128])
@@ -402,7 +404,7 @@ def test_merge_one_long_row_among_short(d_h, nw):
     c = make_case(8200 + d_h + nw, ctx, n_q=8, n_kv=2, d_h=d_h)
     _say(f"merge long row among short d_h={d_h} nw={nw}")
     got, _ = run_case(c, num_partitions=nw)
-    assert max_err(got, c.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got, c.oracle_out()), TOL_16BIT)
 
 
 @pytest.mark.parametrize("nw", [7, 1000])
@@ -416,4 +418,39 @@ def test_merge_nan_piece_poisons_row(nw):
     got, _ = run_case(c, table=t, num_partitions=nw)
     ref = c.oracle_out()
     assert np.isnan(got[1]).all()
-    assert max_err(got[[0, 2]], ref[[0, 2]]) < TOL_16BIT
+    assert_parity(max_err(got[[0, 2]], ref[[0, 2]]), TOL_16BIT)
+
+
+@pytest.mark.parametrize("kv_dtype", [INT8, FP8, BF16])
+@pytest.mark.parametrize("nw", [0, 4])
+def test_unattended_slots_are_never_read(kv_dtype, nw):
+    """Slots that hold no attended position (the tail of each row's last
+    block, and every block no row owns, with its scales) are never read: two
+    runs that differ only there give bit-identical output. The synthetic int8
+    poison is a finite code (-128), so for int8 only this check shows that no
+    stray read happens."""
+    c = make_case(9700 + 10 * kv_dtype + nw, CTX_RAGGED, n_q=8, n_kv=2, d_h=128,
+                  kv_dtype=kv_dtype)
+    _say(f"unattended slots dtype={kv_dtype} nw={nw}")
+    a, _ = run_case(c, num_partitions=nw)
+    assert_parity(max_err(a, c.oracle_out()), TOL_8BIT if kv_dtype in (FP8, INT8) else TOL_16BIT)
+    attended = np.zeros(c.k.shape[:1] + c.k.shape[2:3], dtype=bool)   # [block, offset]
+    for b in range(c.B):
+        for t in range(int(c.ctx[b])):
+            attended[c.table[b, t // c.bs], t % c.bs] = True
+    r = np.random.default_rng(98 + kv_dtype)
+    k2, v2 = c.k.copy(), c.v.copy()
+    for x in (k2, v2):
+        raw = x.view(np.uint8 if x.dtype.itemsize == 1 else np.uint16)
+        noise = r.integers(0, 1 << (8 * x.dtype.itemsize), size=raw.shape).astype(raw.dtype)
+        sel = ~attended[:, None, :, None].repeat(c.n_kv, 1).repeat(c.d_h, 3)
+        raw[sel] = noise[sel]
+    ks2 = vs2 = None
+    if c.k_scale is not None:
+        unowned = ~attended.any(axis=1)
+        ks2, vs2 = c.k_scale.copy(), c.v_scale.copy()
+        ks2[unowned] = r.uniform(0.5, 2.0, size=ks2[unowned].shape).astype(np.float32)
+        vs2[unowned] = r.uniform(0.5, 2.0, size=vs2[unowned].shape).astype(np.float32)
+    c2 = dataclasses.replace(c, k=k2, v=v2, k_scale=ks2, v_scale=vs2)
+    b, _ = run_case(c2, num_partitions=nw)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

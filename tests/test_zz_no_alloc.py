@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from synth import BF16, F32
-from tests.gpu_helpers import TOL_16BIT, max_err, to_dev
+from tests.gpu_helpers import TOL_16BIT, assert_parity, max_err, to_dev
 from tests.helpers import make_case
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,7 @@ def test_noalloc_matches_caller_workspace_on_consecutive_calls():
         got, want, desc = _run_both(case)
         assert pda.attn_workspace_size(desc) > 0          # the split path uses the scratch
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
-        assert max_err(got, case.oracle_out()) < TOL_16BIT
+        assert_parity(max_err(got, case.oracle_out()), TOL_16BIT)
 
 
 def test_noalloc_fp32_cache_and_bf16_output():
@@ -58,7 +58,7 @@ def test_noalloc_fp32_cache_and_bf16_output():
     got, want, desc = _run_both(c32, num_partitions=4)
     assert pda.attn_workspace_size(desc) > 0
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
-    assert max_err(got, c32.oracle_out()) < TOL_16BIT
+    assert_parity(max_err(got, c32.oracle_out()), TOL_16BIT)
     cb = make_case(91_003, [1800, 640], n_q=16, n_kv=4, d_h=128, kv_dtype=BF16)
     got, want, _ = _run_both(cb, out_dtype=BF16)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
