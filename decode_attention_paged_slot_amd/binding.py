@@ -15,7 +15,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpda.so")
+# PDA_LIB names another build of the library to load instead (the test suite
+# loads a host-only sanitizer build this way)
+LIB_PATH = os.environ.get("PDA_LIB") or os.path.join(_HERE, "libpda.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -50,6 +50,7 @@ from __future__ import annotations
 
 import collections
 import ctypes
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -81,9 +82,12 @@ def load(path: str) -> ctypes.CDLL:
 
 
 def lib() -> ctypes.CDLL:
+    """The compiled oracle (PDA_ORACLE_LIB names another build of it, such as
+    the test suite's sanitizer build)."""
     global _lib
     if _lib is None:
-        _lib = load(_build.ensure_built())
+        other = os.environ.get("PDA_ORACLE_LIB")
+        _lib = load(other if other else _build.ensure_built())
     return _lib
 
 
