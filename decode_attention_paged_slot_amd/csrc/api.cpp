@@ -294,6 +294,7 @@ int32_t check_attn_desc(const pda_attn_desc* d, CallKind kind) {
         return PDA_EINVAL;
     }
     if ((int64_t)d->B * d->max_blocks_per_seq > INT32_MAX ||
+        (int64_t)d->num_blocks * d->n_kv > INT32_MAX ||
         (int64_t)d->num_blocks * d->n_kv * kBlockSize * d->d_h * 4 > ((int64_t)1 << 46)) {
         set_error("sizes overflow the supported range");
         return PDA_EINVAL;

@@ -142,6 +142,7 @@ __device__ __forceinline__ uint32_t encode_lane(uint2 w, int src_dtype, float in
 // the row, or its sink and window blocks with a sliding window).
 struct Meta {
     int id;      // physical block, or -1 when the table entry is unmapped
+    int tile;    // (block, head) tile index id * n_kv + j (block 0 when unmapped)
     int info;
     int mask;    // attended positions of the block (bit k: token k)
     float ksc, vsc;
@@ -155,7 +156,8 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     constexpr bool I4 = KV == DT_INT4;   // 4-bit: per-channel K and per-token V scales
     // per wave: the V tile (bf16) and, for bf16 caches, the K tile
     constexpr bool KST = KV == DT_BF16;
-    __shared__ __attribute__((aligned(16))) char stage_all[4 * T::LTILE * (KST ? 2 : 1)];
+    // (the 4-bit kernel stages the V tiles of two blocks per step)
+    __shared__ __attribute__((aligned(16))) char stage_all[4 * T::LTILE * ((KST || I4) ? 2 : 1)];
     // fused decode step: per wave, the new K and V rows (up to 512 B each)
     __shared__ __attribute__((aligned(16))) char newrow_all[4 * 2 * 512];
     __shared__ int wsum[4], wsumu[4];
@@ -176,7 +178,8 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     // blocks, and in split units, where every non-empty segment also counts
     // seg_cost units for its fixed costs (query load, partial write), so that
     // waves crossing many short segments get fewer blocks
-    const int C = a.seg_cost;
+    // (4-bit: no segment cost, so that units are blocks and cuts fall between pairs)
+    const int C = I4 ? 0 : a.seg_cost;
     {
         const int R = (B + kAttnThreads - 1) / kAttnThreads;
         const int r0 = threadIdx.x * R;
@@ -186,7 +189,10 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                                ? (n < 0 || n > a.max_blocks * 16 ? -1 : 0)
                                : row_prefix_len(n, a.prefix_lens[b], a.max_blocks,
                                                 a.prefix_blocks);
-            if (I4) return pl < 0 ? -1 : n / 16;   // encoded blocks; the open one is a piece of its own
+            // 4-bit: the encoded blocks (the open one is a piece of its own),
+            // padded to an even count with one fully masked block, so that
+            // every segment starts at an even position of the block axis
+            if (I4) return pl < 0 ? -1 : ((n / 16) + 1) & ~1;
             return pl < 0 ? -1 : row_blocks(n, a.window, a.sinks).count - pl;
         };
         int local = 0, localu = 0;
@@ -241,7 +247,8 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     const int64_t T_u = (int64_t)n_kv * preu[B];
     // never more ranges than units: every range in use is non-empty, so the
     // pieces of a segment come from consecutive waves without gaps
-    const int NW = (int)max((int64_t)1, min((int64_t)a.nw, T_u));
+    // (4-bit: ranges are cut between pairs of blocks, T_u / 2 pairs)
+    const int NW = (int)max((int64_t)1, min((int64_t)a.nw, I4 ? T_u / 2 : T_u));
     const int wg = blockIdx.x * 4 + wave;   // global wave index
 
     // first block position at or after unit u: segment s of row b spans units
@@ -265,8 +272,13 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     int64_t lo = 0, hi = 0, lo_u = 0, hi_u = 0;
     if (a.split) {
         if (wg < NW) {
-            lo_u = (int64_t)wg * T_u / NW;
-            hi_u = (int64_t)(wg + 1) * T_u / NW;
+            if (I4) {
+                lo_u = 2 * ((int64_t)wg * (T_u / 2) / NW);
+                hi_u = 2 * ((int64_t)(wg + 1) * (T_u / 2) / NW);
+            } else {
+                lo_u = (int64_t)wg * T_u / NW;
+                hi_u = (int64_t)(wg + 1) * T_u / NW;
+            }
             lo = C == 0 ? lo_u : unit_to_block(lo_u);   // with no segment cost, units are blocks
             hi = C == 0 ? hi_u : unit_to_block(hi_u);
         }
@@ -314,7 +326,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 
     // ---- per-block metadata of batch `batch` (64 blocks from lo + 64 * batch)
     auto load_meta = [&](int batch) {
-        Meta m{-1, 0, 0, 1.0f, 1.0f};
+        Meta m{-1, 0, 0, 0, 1.0f, 1.0f};
         const int64_t f = lo + (int64_t)batch * 64 + lane;
         if (f < hi) {
             const int x = (int)f;
@@ -333,19 +345,23 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             // prefix pass, this pass starts after them (no window there)
             const int pl = a.prefix_lens == nullptr ? 0 : a.prefix_lens[b];
             const int blk = row_block_logical(row_blocks(nn[b], a.window, a.sinks), bl) + pl;
-            int id = a.block_table[(int64_t)b * a.max_blocks + blk];
+            // 4-bit: the pad block that evens a segment's block count is
+            // fully masked and reads block 0 (no table lookup, no poison)
+            const bool pad = I4 && bl >= (nn[b] >> 4);
+            int id = pad ? 0 : a.block_table[(int64_t)b * a.max_blocks + blk];
             if (id < 0 || id >= a.num_blocks) id = -1;
             const int seg = b * n_kv + j;
             m.id = id;
+            m.tile = (id < 0 ? 0 : id) * n_kv + j;
             // bit 4: the row's pieces always go to the merge (a shared
             // prefix, or a 4-bit cache's non-empty residual window)
             const bool merged = pl > 0 || (a.extra_pieces > 0 && (nn[b] & 15) != 0);
             m.info = (merged << 4) | ((bl == 0) << 5) | ((bl == nb - 1) << 6) |
                      ((blk < a.reuse_blocks) << 7) | (seg << 8);
-            m.mask = (int)block_token_mask(blk, nn[b], a.window, a.sinks);
+            m.mask = pad ? 0 : (int)block_token_mask(blk, nn[b], a.window, a.sinks);
             if (QUANT && id >= 0) {
-                m.ksc = a.k_scale[(int64_t)id * n_kv + j];
-                m.vsc = a.v_scale[(int64_t)id * n_kv + j];
+                m.ksc = a.k_scale[m.tile];
+                m.vsc = a.v_scale[m.tile];
             }
         }
         return m;
@@ -433,13 +449,17 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     f32x4 acc[T::NT];
 #pragma unroll
     for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-    float w_run = 0.0f;   // 4-bit: sum of the value weights (hi + lo) fed to the PV product
+    // 4-bit: sum of the value weights (hi + lo) fed to the value product, per
+    // head, formed by one more matrix product of the weights with ones (every
+    // row of it holds the column sums), so it costs no vector instructions
+    f32x4 wfed = {0.0f, 0.0f, 0.0f, 0.0f};
     bool piece_bad = false;
     bool piece_whole = false;   // the current piece began at its segment's first block
     int q_seg = -1;
 
     char* stage = stage_all + wave * T::LTILE;
     char* kstage = stage_all + (4 + wave) * T::LTILE;   // used when KST
+    constexpr int kStage2 = 4 * T::LTILE;               // 4-bit: the second V tile, after the first
     const char* kbase = (const char*)a.k;
     const char* vbase = (const char*)a.v;
     const int64_t head_stride = T::TILEB;
@@ -478,14 +498,14 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 
     // metadata of the consumer's batch (A) and of the next one (Bm)
     Meta A = load_meta(0);
-    Meta Bm = cnt > 64 ? load_meta(1) : Meta{-1, 0, 0, 1.0f, 1.0f};
+    Meta Bm = cnt > 64 ? load_meta(1) : Meta{-1, 0, 0, 0, 1.0f, 1.0f};
     int batchA = 0;
-    auto meta_id = [&](int i) {
-        const int v = (i >> 6) == batchA ? A.id : Bm.id;
-        return __builtin_amdgcn_readlane(v, i & 63);
-    };
     auto meta_info = [&](int i) {
         const int v = (i >> 6) == batchA ? A.info : Bm.info;
+        return __builtin_amdgcn_readlane(v, i & 63);
+    };
+    auto meta_tile = [&](int i) {
+        const int v = (i >> 6) == batchA ? A.tile : Bm.tile;
         return __builtin_amdgcn_readlane(v, i & 63);
     };
     auto meta_mask = [&](int i) {
@@ -521,12 +541,12 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     // issues the same instructions and the waits before each block's math
     // only drain that block's loads.
     auto issue = [&](int s, int i) {
-        int pb = meta_id(i);
-        pb = pb < 0 ? 0 : pb;
+        // the (block, head) tile: its index comes with the block's metadata,
+        // so no division by n_kv happens per block
+        const int64_t tile = (uint32_t)meta_tile(i);
         const int info = meta_info(i);
-        const int j = (int)((unsigned)info >> 8) % n_kv;
-        const char* kt = kbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
-        const char* vt = vbase + (int64_t)pb * block_stride + (int64_t)j * head_stride;
+        const char* kt = kbase + tile * head_stride;
+        const char* vt = vbase + tile * head_stride;
         // bf16 K: contiguous 1 KiB per load instruction (staged through LDS
         // into the operand layout); 8-bit K: straight into the operand
         // registers, lane (t, grp) taking 16 B of token row t
@@ -545,7 +565,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 kr[s][0] = make_uint4(kk.x, kk.y, 0, 0);
                 vr[s][0] = make_uint4(vv.x, vv.y, 0, 0);
             }
-            vsr[s] = *(const f32x4*)(a.v_scale + ((int64_t)pb * n_kv + j) * 16 + 4 * grp);
+            vsr[s] = *(const f32x4*)(a.v_scale + tile * 16 + 4 * grp);
             return;
         }
         const int koff = KST ? 16 * lane : col * T::ROWB + 16 * grp;
@@ -578,7 +598,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         float l_tot = sum_rows4(l_run);
         // 4-bit: the V operand holds 136 + code, so the product carries
         // 136 * (sum of the weights it was fed); remove it
-        const float off = I4 ? kInt4Bias * sum_rows4(w_run) : 0.0f;
+        const float off = I4 ? kInt4Bias * wfed[0] : 0.0f;
         if (piece_bad) l_tot = __builtin_nanf("");
         if (col < g) {
             const int64_t prow = whole ? (int64_t)seg * g + col : ((int64_t)seg + wg) * g + col;
@@ -607,10 +627,60 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         }
         m_run = -__builtin_inff();
         l_run = 0.0f;
-        w_run = 0.0f;
+        wfed = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
         piece_bad = false;
+    };
+
+    // a new piece starts at a segment's first block or at the range's first
+    auto piece_start = [&](int seg, bool seg_first) {
+        piece_whole = seg_first;
+        if (seg != q_seg) {
+            load_q(seg);
+            q_seg = seg;
+        }
+        if (a.split && seg_first && lane == 0) {
+            // record the waves covering this segment for the merge: the last
+            // is the wave holding the segment's last unit
+            const int b = seg / n_kv, j = seg - (seg / n_kv) * n_kv;
+            const int64_t end_u =
+                (int64_t)n_kv * preu[b] + (int64_t)(j + 1) * (pre[b + 1] - pre[b] + C);
+            const int last_wave = I4 ? (int)((((end_u - 1) / 2 + 1) * NW - 1) / (T_u / 2))
+                                     : (int)((end_u * NW - 1) / T_u);
+            a.seg_info[seg] = make_int2(wg, last_wave);
+        }
+    };
+
+    // the consumer moves to the next metadata batch when block i lies in it
+    auto enter = [&](int i) {
+        if ((i >> 6) != batchA) {
+            A = Bm;
+            ++batchA;
+            if ((batchA + 1) * 64 < cnt) Bm = load_meta(batchA + 1);
+        }
+    };
+
+    // P split into bf16 hi + lo (the weights keep ~16 bits). Lane (h, G)
+    // holds tokens 4 G .. 4 G + 3 of head h as H_G (hi) and L_G (lo); the
+    // packed B operand needs, per lane row G, k = 8 G .. 8 G + 7 = [H0 H1],
+    // [H2 H3], [L0 L1], [L2 L3]: a permlane32 swap of (H, L) then a
+    // permlane16 swap regroups them.
+    auto pack_p = [&](const float (&w)[4]) -> bf16x8 {
+        uint32_t hi16[4], lo16[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(w[e], hi16[e], lo16[e]);
+        uint32_t H[2] = {hi16[0] | (hi16[1] << 16), hi16[2] | (hi16[3] << 16)};
+        uint32_t L[2] = {lo16[0] | (lo16[1] << 16), lo16[2] | (lo16[3] << 16)};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const auto x = __builtin_amdgcn_permlane32_swap(H[q], L[q], false, false);
+            const auto y = __builtin_amdgcn_permlane16_swap(x[0], x[1], false, false);
+            H[q] = y[0];
+            L[q] = y[1];
+        }
+        const u32x4 pb4 = {H[0], H[1], L[0], L[1]};
+        return __builtin_bit_cast(bf16x8, pb4);
     };
 
     auto consume = [&](int s, int i, bool refill) {
@@ -624,22 +694,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         const bool seg_first = (info >> 5) & 1;
         const bool seg_last = (info >> 6) & 1;
         const int seg = (int)((unsigned)info >> 8);
-        if (seg_first || i == 0) {   // a new piece starts here
-            piece_whole = seg_first;
-            if (seg != q_seg) {
-                load_q(seg);
-                q_seg = seg;
-            }
-            if (a.split && seg_first && lane == 0) {
-                // record the waves covering this segment for the merge: the
-                // last is the wave holding the segment's last unit
-                const int b = seg / n_kv, j = seg - (seg / n_kv) * n_kv;
-                const int64_t end_u =
-                    (int64_t)n_kv * preu[b] + (int64_t)(j + 1) * (pre[b + 1] - pre[b] + C);
-                const int last_wave = (int)((end_u * NW - 1) / T_u);
-                a.seg_info[seg] = make_int2(wg, last_wave);
-            }
-        }
+        if (seg_first || i == 0) piece_start(seg, seg_first);
         // 4-bit value scales of this block, taken before the slot is refilled
         const f32x4 vsb = I4 ? vsr[s] : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
         const int pb_i = cur_id(i);
@@ -743,8 +798,9 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 *(uint4*)(kstage + vrow[l] * T::ROWB +
                           16 * ((lane % T::CPRB) ^ kswz<HD>(vrow[l]))) = kr[s][l];
         }
-        // scores S^T = K . Q^T
-        f32x4 st = {0, 0, 0, 0};
+        // scores S^T = K . Q^T; with a hi + lo query the two passes go to
+        // separate accumulators, two independent chains of matrix products
+        f32x4 st = {0, 0, 0, 0}, stl = {0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < T::NCH; ++c) {
             bf16x8 kop;
@@ -758,8 +814,9 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             }
             st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[c], st, 0, 0, 0);
             if (QT == DT_F32 || I4)
-                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
+                stl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], stl, 0, 0, 0);
         }
+        if (QT == DT_F32 || I4) st += stl;
         // refill this slot with the block kDepth ahead
         if (refill) issue(s, i + kDepth);
 
@@ -789,7 +846,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             const float alpha = m_run == -__builtin_inff() ? 0.0f
                                                            : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
-            w_run *= alpha;
+            if (I4) wfed *= alpha;
 #pragma unroll
             for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
             m_run = m_new;
@@ -803,28 +860,20 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         }
         l_run += psum;
 
-        // P split into bf16 hi + lo (the weights keep ~16 bits). Lane (h, G)
-        // holds tokens 4 G .. 4 G + 3 of head h as H_G (hi) and L_G (lo);
-        // the packed B operand needs, per lane row G, k = 8 G .. 8 G + 7 =
-        // [H0 H1], [H2 H3], [L0 L1], [L2 L3]: a permlane32 swap of (H, L)
-        // then a permlane16 swap regroups them.
-        uint32_t hi16[4], lo16[4];
+        float pw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            split_bf16(pe[e] * (I4 ? vsb[e] : vsc), hi16[e], lo16[e]);
-            if (I4) w_run += __uint_as_float(hi16[e] << 16) + __uint_as_float(lo16[e] << 16);
-        }
-        uint32_t H[2] = {hi16[0] | (hi16[1] << 16), hi16[2] | (hi16[3] << 16)};
-        uint32_t L[2] = {lo16[0] | (lo16[1] << 16), lo16[2] | (lo16[3] << 16)};
+        for (int e = 0; e < 4; ++e) pw[e] = pe[e] * (I4 ? vsb[e] : vsc);
+        if (I4 && mask != 0xFFFFu) {   // the pad block: its scales may be anything
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            const auto x = __builtin_amdgcn_permlane32_swap(H[w], L[w], false, false);
-            const auto y = __builtin_amdgcn_permlane16_swap(x[0], x[1], false, false);
-            H[w] = y[0];
-            L[w] = y[1];
+            for (int e = 0; e < 4; ++e)
+                if (!((mask >> (4 * grp + e)) & 1u)) pw[e] = 0.0f;
         }
-        const u32x4 pb4 = {H[0], H[1], L[0], L[1]};
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, pb4);
+        const bf16x8 pop = pack_p(pw);
+        if constexpr (I4) {
+            const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+            wfed = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), pop,
+                                                           wfed, 0, 0, 0);
+        }
 
         // O^T += [V^T | V^T] . [P_hi ; P_lo]
 #pragma unroll
@@ -836,6 +885,125 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                                                               acc[t], 0, 0, 0);
         }
         if (seg_last || i == cnt - 1) flush(seg, piece_whole && seg_last && !((info >> 4) & 1));
+    };
+
+    // 4-bit cache, steady state: blocks i and i + 1 (slots s and s + 1) of
+    // one piece in one online-softmax step -- two independent chains of
+    // score and value products per wave, and the step's control (maximum,
+    // rescale test, sums) paid once per 32 tokens. Segments have even block
+    // counts and ranges are cut between pairs, so i is even within its
+    // segment and both blocks belong to the same piece; block i is a full
+    // block, block i + 1 full or the segment's masked pad.
+    auto consume_pair = [&](int s, int i) {
+        enter(i);
+        const int info0 = cur_info(i);
+        const int pb0 = cur_id(i);
+        enter(i + 1);
+        const int info1 = cur_info(i + 1);
+        const int pb1 = cur_id(i + 1);
+        const uint32_t mask1 = cur_mask(i + 1);   // 0 for the pad block, else full
+        const bool seg_first = (info0 >> 5) & 1;
+        const bool seg_last = (info1 >> 6) & 1;
+        const int seg = (int)((unsigned)info0 >> 8);
+        if (seg_first || i == 0) piece_start(seg, seg_first);
+        const f32x4 vsb0 = vsr[s], vsb1 = vsr[s + 1];
+        if (pb0 < 0 || pb1 < 0) piece_bad = true;
+        // both V tiles into this wave's two LDS tiles
+        {
+            const uint32_t w0[4] = {vr[s][0].x, vr[s][0].y, vr[s][0].z, vr[s][0].w};
+            const uint32_t w1[4] = {vr[s + 1][0].x, vr[s + 1][0].y, vr[s + 1][0].z,
+                                    vr[s + 1][0].w};
+#pragma unroll
+            for (int c = 0; c < T::LB / 4; ++c) {
+                char* dst = stage + lds_off<HD>(col, (HD / 32) * grp + c);
+                *(bf16x8*)dst = int4x8_to_bf16_biased(w0[c]);
+                *(bf16x8*)(dst + kStage2) = int4x8_to_bf16_biased(w1[c]);
+            }
+        }
+        // scores of both blocks: two independent chains (the hi and lo
+        // query passes of each block accumulate together)
+        f32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+        {
+            const uint32_t k0[4] = {kr[s][0].x, kr[s][0].y, kr[s][0].z, kr[s][0].w};
+            const uint32_t k1[4] = {kr[s + 1][0].x, kr[s + 1][0].y, kr[s + 1][0].z,
+                                    kr[s + 1][0].w};
+#pragma unroll
+            for (int c = 0; c < T::NCH; ++c) {
+                const bf16x8 a0 = int4x8_to_bf16_biased(k0[c]);
+                const bf16x8 a1 = int4x8_to_bf16_biased(k1[c]);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qhi[c], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qhi[c], s1, 0, 0, 0);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qlo[c], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qlo[c], s1, 0, 0, 0);
+            }
+        }
+        issue(s, i + kDepth);
+        issue(s + 1, i + 1 + kDepth);
+
+        // online softmax over the step's 32 tokens (base-2 domain)
+        const float mult = a.scale_log2;
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = (s0[e] - cq) * mult;
+            sv[4 + e] = mask1 != 0 ? (s1[e] - cq) * mult : -__builtin_inff();
+        }
+        const float lmx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        if (__builtin_amdgcn_ballot_w64(lmx > m_run + kSlack) != 0) {   // as in consume
+            const float mx = max_rows4(lmx);
+            const float m_new = mx > m_run + kSlack ? mx : m_run;
+            const float alpha = m_run == -__builtin_inff() ? 0.0f
+                                                           : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            wfed *= alpha;
+#pragma unroll
+            for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+        float pe[8], psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+            psum += pe[e];
+        }
+        l_run += psum;
+        float w0[4], w1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w0[e] = pe[e] * vsb0[e];
+            w1[e] = mask1 != 0 ? pe[4 + e] * vsb1[e] : 0.0f;
+        }
+        const bf16x8 p0 = pack_p(w0), p1 = pack_p(w1);
+        const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        wfed = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), p0, wfed,
+                                                       0, 0, 0);
+        wfed = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), p1, wfed,
+                                                       0, 0, 0);
+        // O^T += [V0^T | V0^T] . [P0_hi ; P0_lo] + [V1^T | V1^T] . [P1_hi ; P1_lo]
+#pragma unroll
+        for (int t = 0; t < T::NT; ++t) {
+            const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)trd0[t]);
+            const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)trd1[t]);
+            // the second tile's addresses: kStage2 past the first (added at
+            // the read, where it becomes the instruction's offset, so no
+            // second set of address registers stays live)
+            uint32_t ab0 = trd0[t], ab1 = trd1[t];
+            asm volatile("" : "+v"(ab0), "+v"(ab1));
+            const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(uintptr_t)(ab0 + kStage2));
+            const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(uintptr_t)(ab1 + kStage2));
+            const s16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const s16x8 vb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), p0,
+                                                              acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vb), p1,
+                                                              acc[t], 0, 0, 0);
+        }
+        if (seg_last || i + 1 == cnt - 1)
+            flush(seg, piece_whole && seg_last && !((info1 >> 4) & 1));
     };
 
     // the first segment's queries, in flight with the first tiles
@@ -853,8 +1021,14 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             __builtin_amdgcn_sched_barrier(0);
         }
         for (; it + 2 * kDepth <= cnt; it += kDepth) {
+            if constexpr (I4) {
+                static_assert(kDepth % 2 == 0, "4-bit steps take blocks in pairs");
 #pragma unroll
-            for (int s = 0; s < kDepth; ++s) consume(s, it + s, true);
+                for (int s = 0; s < kDepth; s += 2) consume_pair(s, it + s);
+            } else {
+#pragma unroll
+                for (int s = 0; s < kDepth; ++s) consume(s, it + s, true);
+            }
         }
     } else {
 #pragma unroll
