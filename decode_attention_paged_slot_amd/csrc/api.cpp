@@ -52,10 +52,10 @@ void set_error(const char* fmt, ...) {
     va_end(ap);
 }
 
-// Partition plan (fp32 caches). The grid is (P, n_q, B) with one workgroup
-// of 4 waves per cell; aim at ~2048 workgroups with 32..256 blocks per
-// partition, so every wave streams at least 8 blocks and the partial results
-// stay below 1% of the cache bytes.
+// Partition plan (fp32 caches). The grid is (P, n_kv, B) with one workgroup
+// of 4 waves per cell serving the g query heads of its KV head; aim at ~2048
+// workgroups with 32..256 blocks per partition, so every wave streams at
+// least 8 blocks and the partial results stay below 1% of the cache bytes.
 Plan make_partition_plan(const pda_attn_desc& d) {
     const int64_t max_ctx = std::max<int64_t>(d.max_context, 1);
     const int32_t nblk_max =
@@ -68,7 +68,7 @@ Plan make_partition_plan(const pda_attn_desc& d) {
     } else {
         const int64_t ctx_blocks = d.total_context > 0 ? ceil_div(d.total_context, d.block_size)
                                                        : (int64_t)d.B * nblk_max;
-        const int64_t tiles = ctx_blocks * d.n_q;
+        const int64_t tiles = ctx_blocks * d.n_kv;
         bpp = ceil_div(tiles, 2048);
         bpp = std::max(bpp, 32);
         bpp = std::min(bpp, 256);

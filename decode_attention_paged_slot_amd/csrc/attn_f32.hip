@@ -7,11 +7,18 @@
 // sinks, section 9.7). Here everything stays in fp32 FMAs; this path serves fp32
 // caches (small, latency-bound workloads), so it favours plainness.
 //
-// grid = (P partitions, n_q, B); one workgroup (4 waves) per query head and
-// partition; wave w takes blocks w, w + 4, ... of the partition. In a wave,
-// lane (t = lane / 4, part = lane % 4) holds token t of the block and the
-// 16-byte column groups part, part + 4, ... of d_h (each load instruction
-// reads 64 contiguous bytes of every row).
+// grid = (P partitions, n_kv, B): one workgroup (4 waves) per KV head of a
+// row and partition serves all g = n_q / n_kv query heads of the group, so
+// each K/V tile is read once per step (grouped-query attention: the query
+// heads of a group address one stored KV head -- GQA teaser on the kv-cache
+// tag page). Wave w takes head lane hg = w % HG (heads hg, hg + HG, ...) and
+// block lane bl = w / HG (blocks bl, bl + BL, ... of the partition), with
+// HG = min(g, 4) and BL = 4 / HG: for g >= 4 the four waves stream the same
+// blocks (the tile comes from HBM once and from cache for the others), for
+// g = 1 they split the blocks. In a wave, lane (t = lane / 4, part =
+// lane % 4) holds token t of the block and the 16-byte column groups part,
+// part + 4, ... of d_h (each load instruction reads 64 contiguous bytes of
+// every row). The queries of the group wait in LDS.
 #include "device_common.h"
 #include "pda_internal.h"
 
@@ -21,18 +28,23 @@ namespace {
 
 __device__ __forceinline__ float fshfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
-template <int HD>
+template <int HD, int NH>
 __global__ void __launch_bounds__(kAttnThreads) k_attn_f32(AttnArgs a) {
     constexpr int NV = HD / 16;   // float4 groups per lane
-    __shared__ float red_o[4][HD];
-    __shared__ float red_ml[4][2];
+    __shared__ float q_sh[4 * NH][HD];
+    __shared__ float red_o[4][NH][HD];
+    __shared__ float red_ml[4][NH][2];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int t = lane >> 2, part = lane & 3;
-    const int b = blockIdx.z, h = blockIdx.y, p = blockIdx.x;
-    const int j = h / a.g;
-    const int64_t row = (int64_t)b * a.n_q + h;
+    const int b = blockIdx.z, j = blockIdx.y, p = blockIdx.x;
+    const int g = a.g;
+    const int HG = g < 4 ? g : 4, BL = 4 / HG;
+    const int hg = wave % HG, bl = wave / HG;
+    const bool idle = wave >= HG * BL;   // g = 3: the fourth wave has no head lane
+    const int nh = idle ? 0 : (g - hg + HG - 1) / HG;   // heads hg, hg + HG, ... < g
+    const int64_t row0 = (int64_t)b * a.n_q + (int64_t)j * g;   // output row of head 0
 
     const int n = a.context_lens[b];
     const bool row_bad = n < 0 || n > a.max_blocks * 16;
@@ -41,37 +53,36 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_f32(AttnArgs a) {
     if (row_bad || blk0 >= nblk) {
         if (a.P == 1) {
             const float v = row_bad ? __builtin_nanf("") : 0.0f;
-            for (int d = threadIdx.x; d < HD; d += kAttnThreads) {
-                if (a.out_dtype == DT_F32) ((float*)a.out)[row * HD + d] = v;
-                else ((uint16_t*)a.out)[row * HD + d] = (uint16_t)f32_to_bf16_rne(v);
+            for (int d = threadIdx.x; d < g * HD; d += kAttnThreads) {
+                if (a.out_dtype == DT_F32) ((float*)a.out)[row0 * HD + d] = v;
+                else ((uint16_t*)a.out)[row0 * HD + d] = (uint16_t)f32_to_bf16_rne(v);
             }
         }
         return;
     }
     const int blk1 = (p == a.P - 1) ? nblk : min(nblk, blk0 + a.bpp);
 
-    float q[NV][4];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int d = 4 * (part + 4 * k);
-        if (a.q_dtype == DT_F32) {
-            const float4 x = *(const float4*)((const float*)a.q + row * HD + d);
-            q[k][0] = x.x; q[k][1] = x.y; q[k][2] = x.z; q[k][3] = x.w;
-        } else {
-            const uint2 w = *(const uint2*)((const uint16_t*)a.q + row * HD + d);
-            q[k][0] = bf16_lo_to_f32(w.x); q[k][1] = bf16_hi_to_f32(w.x);
-            q[k][2] = bf16_lo_to_f32(w.y); q[k][3] = bf16_hi_to_f32(w.y);
-        }
+    // the group's queries into LDS (fp32)
+    for (int d = threadIdx.x; d < g * HD; d += kAttnThreads) {
+        q_sh[d / HD][d % HD] = a.q_dtype == DT_F32
+                                   ? ((const float*)a.q)[row0 * HD + d]
+                                   : bf16_lo_to_f32(((const uint16_t*)a.q)[row0 * HD + d]);
     }
+    __syncthreads();
 
-    float m_run = -__builtin_inff(), l_run = 0.0f;
-    float acc[NV][4];
+    float m_run[NH], l_run[NH];
+    float acc[NH][NV][4];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.0f;
+    for (int k = 0; k < NH; ++k) {
+        m_run[k] = -__builtin_inff();
+        l_run[k] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[k][v][0] = acc[k][v][1] = acc[k][v][2] = acc[k][v][3] = 0.0f;
+    }
     bool bad = false;
     const int64_t tile = 16 * HD;   // floats per (block, head) tile
 
-    for (int kb = blk0 + wave; kb < blk1; kb += 4) {
+    for (int kb = blk0 + bl; !idle && kb < blk1; kb += BL) {
         // attended positions of the block (all t < n, or the window / sinks);
         // a block without any is never looked up
         const uint32_t bm = block_token_mask(kb, n, a.window, a.sinks);
@@ -81,88 +92,109 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_f32(AttnArgs a) {
         const bool live = (bm >> t) & 1u;
         const float* kt = (const float*)a.k + ((int64_t)pb * a.n_kv + j) * tile + t * HD;
         const float* vt = (const float*)a.v + ((int64_t)pb * a.n_kv + j) * tile + t * HD;
-        // fused decode step: position n - 1 takes the new token's K/V (all
-        // query heads of the group use it; the group's first head writes it)
+        // fused decode step: position n - 1 takes the new token's K/V (every
+        // head of the group uses it; the waves of head lane 0 write it)
         const bool fresh = a.k_new != nullptr && 16 * kb + t == n - 1;
         const float* kn = (const float*)a.k_new + ((int64_t)b * a.n_kv + j) * HD;
         const float* vn = (const float*)a.v_new + ((int64_t)b * a.n_kv + j) * HD;
         float kv[NV][4], vv[NV][4];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
+        for (int v = 0; v < NV; ++v) {
             float4 x = make_float4(0, 0, 0, 0), y = make_float4(0, 0, 0, 0);
             if (fresh) {
-                x = *(const float4*)(kn + 4 * (part + 4 * k));
-                y = *(const float4*)(vn + 4 * (part + 4 * k));
-                if (h % a.g == 0) {
-                    *(float4*)(kt + 4 * (part + 4 * k)) = x;
-                    *(float4*)(vt + 4 * (part + 4 * k)) = y;
+                x = *(const float4*)(kn + 4 * (part + 4 * v));
+                y = *(const float4*)(vn + 4 * (part + 4 * v));
+                if (hg == 0) {
+                    *(float4*)(kt + 4 * (part + 4 * v)) = x;
+                    *(float4*)(vt + 4 * (part + 4 * v)) = y;
                 }
             } else if (live) {
-                x = *(const float4*)(kt + 4 * (part + 4 * k));
-                y = *(const float4*)(vt + 4 * (part + 4 * k));
+                x = *(const float4*)(kt + 4 * (part + 4 * v));
+                y = *(const float4*)(vt + 4 * (part + 4 * v));
             }
-            kv[k][0] = x.x; kv[k][1] = x.y; kv[k][2] = x.z; kv[k][3] = x.w;
-            vv[k][0] = y.x; vv[k][1] = y.y; vv[k][2] = y.z; vv[k][3] = y.w;
+            kv[v][0] = x.x; kv[v][1] = x.y; kv[v][2] = x.z; kv[v][3] = x.w;
+            vv[v][0] = y.x; vv[v][1] = y.y; vv[v][2] = y.z; vv[v][3] = y.w;
         }
-        float dot = 0.0f;
 #pragma unroll
-        for (int k = 0; k < NV; ++k)
+        for (int k = 0; k < NH; ++k) {
+            if (k >= nh) break;
+            const float* qh = q_sh[hg + HG * k];
+            float dot = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dot = fmaf(q[k][e], kv[k][e], dot);
-        dot += fshfl_xor(dot, 1);
-        dot += fshfl_xor(dot, 2);
-        const float s = live ? dot * a.scale_log2 : -__builtin_inff();
-        float mx = s;
-        mx = fmaxf(mx, fshfl_xor(mx, 4));
-        mx = fmaxf(mx, fshfl_xor(mx, 8));
-        mx = fmaxf(mx, fshfl_xor(mx, 16));
-        mx = fmaxf(mx, fshfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        const float pr = __builtin_amdgcn_exp2f(s - m_use);
-        l_run = l_run * alpha + (part == 0 ? pr : 0.0f);
-        m_run = m_new;
+            for (int v = 0; v < NV; ++v) {
+                const float4 qv = *(const float4*)(qh + 4 * (part + 4 * v));
+                dot = fmaf(qv.x, kv[v][0], dot);
+                dot = fmaf(qv.y, kv[v][1], dot);
+                dot = fmaf(qv.z, kv[v][2], dot);
+                dot = fmaf(qv.w, kv[v][3], dot);
+            }
+            dot += fshfl_xor(dot, 1);
+            dot += fshfl_xor(dot, 2);
+            const float s = live ? dot * a.scale_log2 : -__builtin_inff();
+            float mx = s;
+            mx = fmaxf(mx, fshfl_xor(mx, 4));
+            mx = fmaxf(mx, fshfl_xor(mx, 8));
+            mx = fmaxf(mx, fshfl_xor(mx, 16));
+            mx = fmaxf(mx, fshfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[k], mx);
+            const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[k] - m_use);
+            const float pr = __builtin_amdgcn_exp2f(s - m_use);
+            l_run[k] = l_run[k] * alpha + (part == 0 ? pr : 0.0f);
+            m_run[k] = m_new;
 #pragma unroll
-        for (int k = 0; k < NV; ++k)
+            for (int v = 0; v < NV; ++v)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(pr, vv[k][e], acc[k][e] * alpha);
+                for (int e = 0; e < 4; ++e) acc[k][v][e] = fmaf(pr, vv[v][e], acc[k][v][e] * alpha);
+        }
     }
 
-    // reduce over the 16 token lanes (and l over all lanes)
+    // per head: reduce over the 16 token lanes (and l over all lanes), then
+    // over the block lanes of the head through LDS
 #pragma unroll
-    for (int k = 0; k < NV; ++k)
+    for (int k = 0; k < NH; ++k) {
+        if (k >= nh) break;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float v = acc[k][e];
-            v += fshfl_xor(v, 4);
-            v += fshfl_xor(v, 8);
-            v += fshfl_xor(v, 16);
-            v += fshfl_xor(v, 32);
-            acc[k][e] = v;
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = acc[k][v][e];
+                x += fshfl_xor(x, 4);
+                x += fshfl_xor(x, 8);
+                x += fshfl_xor(x, 16);
+                x += fshfl_xor(x, 32);
+                acc[k][v][e] = x;
+            }
+        float l_tot = l_run[k];
+        for (int m = 1; m < 64; m <<= 1) l_tot += fshfl_xor(l_tot, m);
+        if (bad) l_tot = __builtin_nanf("");
+        if (t == 0) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) red_o[wave][k][4 * (part + 4 * v) + e] = acc[k][v][e];
         }
-    float l_tot = l_run;
-    for (int m = 1; m < 64; m <<= 1) l_tot += fshfl_xor(l_tot, m);
-    if (bad) l_tot = __builtin_nanf("");
-    if (t == 0) {
-#pragma unroll
-        for (int k = 0; k < NV; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) red_o[wave][4 * (part + 4 * k) + e] = acc[k][e];
+        if (lane == 0) {
+            red_ml[wave][k][0] = m_run[k];
+            red_ml[wave][k][1] = l_tot;
+        }
     }
-    if (lane == 0) { red_ml[wave][0] = m_run; red_ml[wave][1] = l_tot; }
     __syncthreads();
-    for (int d = threadIdx.x; d < HD; d += kAttnThreads) {
+    for (int x = threadIdx.x; x < g * HD; x += kAttnThreads) {
+        const int hh = x / HD, d = x - (x / HD) * HD;
+        const int hl = hh % HG, k = hh / HG;   // head lane and its local head
         float M = -__builtin_inff();
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[w][0]);
+        for (int q = 0; q < BL; ++q) M = fmaxf(M, red_ml[hl + HG * q][k][0]);
         float L = 0.0f, o = 0.0f;
-        for (int w = 0; w < 4; ++w) {
-            const float sc = red_ml[w][0] == -__builtin_inff() ? 0.0f
-                                                               : __builtin_amdgcn_exp2f(red_ml[w][0] - M);
-            L += sc * red_ml[w][1];
-            o += sc * red_o[w][d];
+        for (int q = 0; q < BL; ++q) {
+            const int w = hl + HG * q;
+            const float sc = red_ml[w][k][0] == -__builtin_inff()
+                                 ? 0.0f : __builtin_amdgcn_exp2f(red_ml[w][k][0] - M);
+            L += sc * red_ml[w][k][1];
+            o += sc * red_o[w][k][d];
         }
         const float r = L != 0.0f ? o / L : 0.0f;
+        const int64_t row = row0 + hh;
         if (a.P > 1) {
             a.part_o[(row * a.P + p) * HD + d] = r;
             if (d == 0) {
@@ -180,9 +212,20 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_f32(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
-    dim3 grid(a.P, a.n_q, a.B);
-    if (a.d_h == 128) hipLaunchKernelGGL((k_attn_f32<128>), grid, dim3(kAttnThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_f32<64>), grid, dim3(kAttnThreads), 0, s, a);
+    dim3 grid(a.P, a.n_kv, a.B);
+    // local heads per wave: ceil(g / min(g, 4))
+    const int nh = a.g <= 4 ? 1 : (a.g <= 8 ? 2 : 4);
+#define PDA_F32(HD, NH) hipLaunchKernelGGL((k_attn_f32<HD, NH>), grid, dim3(kAttnThreads), 0, s, a)
+    if (a.d_h == 128) {
+        if (nh == 1) PDA_F32(128, 1);
+        else if (nh == 2) PDA_F32(128, 2);
+        else PDA_F32(128, 4);
+    } else {
+        if (nh == 1) PDA_F32(64, 1);
+        else if (nh == 2) PDA_F32(64, 2);
+        else PDA_F32(64, 4);
+    }
+#undef PDA_F32
     return hipGetLastError();
 }
 

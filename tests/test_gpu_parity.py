@@ -135,6 +135,18 @@ def test_fp32_cache(q_dtype, d_h):
     assert_parity(max_err(got2, c.oracle_out()), TOL_16BIT)
 
 
+@pytest.mark.parametrize("g", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("nparts", [0, 1, 4])
+def test_fp32_cache_query_groups(g, nparts):
+    """fp32 caches: one workgroup per (partition, KV head, row) serves all g
+    query heads of the group (head lanes and block lanes of its waves)."""
+    c = make_case(3200 + 10 * g + nparts, CTX_RAGGED, n_q=2 * g, n_kv=2, d_h=128,
+                  kv_dtype=F32, q_dtype=F32)
+    _say(f"fp32 cache g={g} partitions={nparts}")
+    got, _ = run_case(c, num_partitions=nparts)
+    assert_parity(max_err(got, c.oracle_out()), TOL_16BIT)
+
+
 @pytest.mark.parametrize("kv_dtype", [FP8, INT8])
 @pytest.mark.parametrize("d_h", [64, 128])
 @pytest.mark.parametrize("g", [1, 4, 8])
