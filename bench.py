@@ -385,10 +385,15 @@ def setup_calls(w, args, dev, inp, shared, table, slots):
         else:
             attend = pda.paged_decode_attn(inp.q, kc, vc, bt, cl, scale, out, desc=desc,
                                            workspace=ws, bind=True)
-    fused = args.fused and not int4   # the 4-bit cache appends and attends in two calls
+    fused = args.fused
     if fused:
         # one launch: each row's new K/V land at position n - 1, then attention
-        if cascade:
+        # (4-bit: the attention launch also does the append, then the merge)
+        if int4:
+            step1 = pda.decode_step_int4(inp.q, inp.k_new, inp.v_new, kc, vc, ks, vs, inp.k_res,
+                                         inp.v_res, bt, cl, scale, out, desc=desc, workspace=ws,
+                                         bind=True)
+        elif cascade:
             step1 = pda.decode_step_prefix(inp.q, inp.k_new, inp.v_new, kc, vc, ks, vs, bt, cl,
                                            pt, pls, scale, out, desc=desc, workspace=ws,
                                            bind=True)

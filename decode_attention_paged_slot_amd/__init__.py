@@ -20,7 +20,7 @@ _BINDING_NAMES = (
     "attn_desc", "attn_workspace_size", "attn_plan", "workspace_for",
     "paged_decode_attn", "paged_decode_attn_quant", "lse_merge",
     "decode_step", "decode_step_quant", "paged_decode_attn_prefix", "decode_step_prefix",
-    "kv_append_int4", "paged_decode_attn_int4", "hbm_read_probe", "BoundCall",
+    "kv_append_int4", "paged_decode_attn_int4", "decode_step_int4", "hbm_read_probe", "BoundCall",
     "paged_decode_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
 )
 

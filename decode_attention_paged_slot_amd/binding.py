@@ -105,6 +105,9 @@ _SIGS = {
     "pda_paged_decode_attn_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           ctypes.c_float, _vp, ctypes.POINTER(AttnDesc), _vp,
                                           _sz, _vp]),
+    "pda_decode_step_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    ctypes.c_float, _vp, ctypes.POINTER(AttnDesc), _vp, _sz,
+                                    _vp]),
     "pda_hbm_read_probe": (_i32, [_vp, _sz, _vp, _i64, _i32, _i32, _vp, _vp]),
     "pda_paged_decode_attn_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                              ctypes.POINTER(AttnDesc), _vp]),
@@ -551,6 +554,31 @@ def paged_decode_attn_int4(q, k_q, v_q, k_scale, v_scale, k_res, v_res, block_ta
                     desc, _ptr(workspace), ws_bytes, _stream(stream)),
                    (q, k_q, v_q, k_scale, v_scale, k_res, v_res, block_table, context_lens, out,
                     workspace), bind)
+
+
+def decode_step_int4(q, k_new, v_new, k_q, v_q, k_scale, v_scale, k_res, v_res, block_table,
+                     context_lens, scale: float, out, *, desc: AttnDesc, workspace=None,
+                     stream=None, bind=False):
+    """pda_decode_step_int4: kv_append_int4 and paged_decode_attn_int4 in
+    one launch pair (context_lens count the new token; k_new, v_new [B, n_kv,
+    d_h] bf16, desc.new_dtype = BF16). Same bits as the two calls."""
+    torch = _torch()
+    if desc.new_dtype != BF16:
+        raise ValueError("a fused 4-bit step takes bf16 k_new / v_new (desc.new_dtype = BF16)")
+    workspace, ws_bytes = _ws(desc, q, workspace)
+    _check_attn(desc, q, k_q, v_q, block_table, context_lens, out, k_scale, v_scale, workspace,
+                quant=True)
+    _int4_state(desc, k_res, v_res, q.device)
+    shape = (desc.B, desc.n_kv, desc.d_h)
+    _need(k_new, "k_new", (torch.bfloat16,), q.device, shape=shape)
+    _need(v_new, "v_new", (torch.bfloat16,), q.device, shape=shape)
+    return _launch("pda_decode_step_int4",
+                   (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_q), _ptr(v_q), _ptr(k_scale),
+                    _ptr(v_scale), _ptr(k_res), _ptr(v_res), _ptr(block_table),
+                    _ptr(context_lens), float(scale), _ptr(out), desc, _ptr(workspace),
+                    ws_bytes, _stream(stream)),
+                   (q, k_new, v_new, k_q, v_q, k_scale, v_scale, k_res, v_res, block_table,
+                    context_lens, out, workspace), bind)
 
 
 def lse_merge(part_o, part_ml, out, *, stream=None, bind=False):

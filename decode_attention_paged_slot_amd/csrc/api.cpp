@@ -672,6 +672,26 @@ int32_t pda_paged_decode_attn_int4(const void* q, const void* k_q, const void* v
                     k_res, v_res);
 }
 
+int32_t pda_decode_step_int4(const void* q, const void* k_new, const void* v_new, void* k_q,
+                             void* v_q, const float* k_scale, float* v_scale, void* k_res,
+                             void* v_res, const int32_t* block_table,
+                             const int32_t* context_lens, float scale, void* out,
+                             const pda_attn_desc* d, void* workspace, size_t ws_bytes,
+                             void* stream) {
+    if (d && d->new_dtype != PDA_BF16) {
+        set_error("a fused 4-bit step takes bf16 k_new / v_new (new_dtype %d)", d->new_dtype);
+        return PDA_EINVAL;
+    }
+    if ((k_res && !aligned16(k_res)) || (v_res && !aligned16(v_res)) ||
+        (k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale))) {
+        set_error("k_res, v_res, k_scale and v_scale must be 16-byte aligned");
+        return PDA_EINVAL;
+    }
+    return run_attn(q, k_q, v_q, k_scale, v_scale, block_table, context_lens, scale, out, d,
+                    workspace, ws_bytes, stream, kInt4, k_new, v_new, true, nullptr, nullptr,
+                    k_res, v_res);
+}
+
 int32_t pda_kv_append_int4(const void* k_new, const void* v_new, const int32_t* block_table,
                            const int32_t* context_lens, void* k_q, void* v_q,
                            const float* k_scale, float* v_scale, void* k_res, void* v_res,

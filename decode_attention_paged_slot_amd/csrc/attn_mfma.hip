@@ -297,6 +297,102 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         }
     };
 
+    // ---- fused 4-bit decode step: the append's work (the 4-bit cache's
+    // append path with its residual window, SoK paper section 2.3), done by
+    // the waves that own it before they stream. The new token of (row b,
+    // KV head j) goes to residual slot (n - 1) % 16 (a bit copy); when it
+    // fills the block, the block's 16 tokens (15 residual rows and the new
+    // one) are encoded into the cache: keys with the per-channel scales,
+    // values with one scale per token (amax / 7 over the token's channels,
+    // 1 if that is 0 or not finite), codes RNE(x * fp32(1 / s)) clamped to
+    // [-7, 7]. The arithmetic is the separate append's, so both give the
+    // same bits.
+    auto resid_write = [&](int b, int j) {
+        const int r = (nn[b] - 1) & 15;
+        const int64_t sj = (int64_t)b * n_kv + j;
+        const uint32_t* kn = (const uint32_t*)a.k_new + sj * (HD / 2);
+        const uint32_t* vn = (const uint32_t*)a.v_new + sj * (HD / 2);
+        uint32_t* kd = (uint32_t*)a.k_res + (sj * 16 + r) * (HD / 2);
+        uint32_t* vd = (uint32_t*)a.v_res + (sj * 16 + r) * (HD / 2);
+        for (int x = lane; x < HD / 2; x += 64) {
+            kd[x] = kn[x];
+            vd[x] = vn[x];
+        }
+    };
+    // encode the block completed by the new token of (b, j) into physical
+    // block pb: lane (token t = col, quarter grp) encodes channels
+    // grp * d_h / 4 .. +d_h / 4 of token t, the bytes it streams later
+    auto encode_fill = [&](int b, int j, int pb) {
+        constexpr int CPL = HD / 4;   // channels per lane
+        float* kinv = (float*)(stage_all + wave * T::LTILE);   // fp32(1 / k_scale), this wave's stage
+        for (int c = lane; c < HD; c += 64) kinv[c] = __fdiv_rn(1.0f, a.k_scale[(int64_t)j * HD + c]);
+        const int64_t sj = (int64_t)b * n_kv + j;
+        const uint16_t* ks = (col == 15 ? (const uint16_t*)a.k_new + sj * HD
+                                        : (const uint16_t*)a.k_res + (sj * 16 + col) * HD) + grp * CPL;
+        const uint16_t* vs = (col == 15 ? (const uint16_t*)a.v_new + sj * HD
+                                        : (const uint16_t*)a.v_res + (sj * 16 + col) * HD) + grp * CPL;
+        float kx[CPL], vx[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL / 8; ++q) {
+            const uint4 kw = *(const uint4*)(ks + 8 * q);
+            const uint4 vw = *(const uint4*)(vs + 8 * q);
+            const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kx[8 * q + 2 * e] = bf16_lo_to_f32(ka[e]);
+                kx[8 * q + 2 * e + 1] = bf16_hi_to_f32(ka[e]);
+                vx[8 * q + 2 * e] = bf16_lo_to_f32(va[e]);
+                vx[8 * q + 2 * e + 1] = bf16_hi_to_f32(va[e]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): kinv is in LDS
+        __builtin_amdgcn_wave_barrier();
+        uint32_t kp[CPL / 8], vp[CPL / 8];
+#pragma unroll
+        for (int q = 0; q < CPL / 8; ++q) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = grp * CPL + 8 * q + i;
+                const uint32_t lo = quant_int4_nibble(__fmul_rn(kx[8 * q + i], kinv[c]));
+                const uint32_t hi = quant_int4_nibble(__fmul_rn(kx[8 * q + 4 + i], kinv[c + 4]));
+                w |= (lo | (hi << 4)) << (8 * i);
+            }
+            kp[q] = w;
+        }
+        float amax = 0.0f, nf = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float v = fabsf(vx[c]);
+            if (!(v <= 3.402823466e38f)) nf = 1.0f;   // NaN or infinite
+            amax = fmaxf(amax, v);
+        }
+        amax = max_rows4(amax);   // the token's four lanes
+        nf = max_rows4(nf);
+        const float sc = (nf == 0.0f && amax > 0.0f) ? __fdiv_rn(amax, 7.0f) : 1.0f;
+        const float inv = __fdiv_rn(1.0f, sc);
+#pragma unroll
+        for (int q = 0; q < CPL / 8; ++q) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = quant_int4_nibble(__fmul_rn(vx[8 * q + i], inv));
+                const uint32_t hi = quant_int4_nibble(__fmul_rn(vx[8 * q + 4 + i], inv));
+                w |= (lo | (hi << 4)) << (8 * i);
+            }
+            vp[q] = w;
+        }
+        const int64_t tbyte = ((int64_t)pb * n_kv + j) * T::TILEB + col * T::ROWB + grp * T::LB;
+        if constexpr (CPL / 8 == 4) {
+            *(uint4*)((char*)a.k + tbyte) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
+            *(uint4*)((char*)a.v + tbyte) = make_uint4(vp[0], vp[1], vp[2], vp[3]);
+        } else {
+            *(uint2*)((char*)a.k + tbyte) = make_uint2(kp[0], kp[1]);
+            *(uint2*)((char*)a.v + tbyte) = make_uint2(vp[0], vp[1]);
+        }
+        if (grp == 0) ((float*)a.v_scale)[((int64_t)pb * n_kv + j) * 16 + col] = sc;
+    };
+
     // ---- sequences without blocks (empty, or invalid length): zero / NaN rows.
     // Split mode: such a sequence sits at unit n_kv * preu[b]; the wave whose
     // unit range holds it owns it (the last wave also owns the unit T_u).
@@ -315,6 +411,9 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 write_rows((int64_t)b * a.n_q, a.n_q, nn[b] < 0 ? __builtin_nanf("") : 0.0f);
                 for (int jj = lane; jj < n_kv; jj += 64)
                     a.seg_info[(int64_t)b * n_kv + jj] = make_int2(0, -1);
+                // fused 4-bit step: a row shorter than a block still appends
+                if (I4 && a.k_new != nullptr && nn[b] > 0)
+                    for (int jj = 0; jj < n_kv; ++jj) resid_write(b, jj);
             }
         }
     } else if (wg < B * n_kv && hi == lo) {
@@ -323,6 +422,39 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 
     const int cnt = (int)(hi - lo);
     if (cnt <= 0) return;
+
+    // fused 4-bit step, the segments this wave streams: the wave holding a
+    // segment's first block writes its new token to the residual window, and
+    // the wave holding a block the new token completes encodes it before
+    // streaming (its stores are complete before its own loads of the tile)
+    if (I4 && a.k_new != nullptr) {
+        bool wrote = false;
+        for (int64_t pos = lo; pos < hi;) {
+            int l = 0, r = B - 1;   // the sequence holding position pos
+            while (l < r) {
+                const int mid = (l + r + 1) >> 1;
+                if ((int64_t)n_kv * pre[mid] <= pos) l = mid;
+                else r = mid - 1;
+            }
+            const int b = l, nb = pre[b + 1] - pre[b];
+            const int j = (int)((pos - (int64_t)n_kv * pre[b]) / nb);
+            const int64_t S = (int64_t)n_kv * pre[b] + (int64_t)j * nb;   // segment start
+            if (S >= lo) resid_write(b, j);
+            const int n = nn[b];
+            if (n >= 16 && (n & 15) == 0) {
+                const int64_t F = S + (n >> 4) - 1;   // the block the new token completes
+                if (F >= lo && F < hi) {
+                    const int pb = a.block_table[(int64_t)b * a.max_blocks + (n >> 4) - 1];
+                    if (pb >= 0 && pb < a.num_blocks) {
+                        encode_fill(b, j, pb);
+                        wrote = true;
+                    }
+                }
+            }
+            pos = S + nb;
+        }
+        if (wrote) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
 
     // ---- per-block metadata of batch `batch` (64 blocks from lo + 64 * batch)
     auto load_meta = [&](int batch) {

@@ -415,8 +415,9 @@ int32_t pda_decode_step_prefix(const void* q, const void* k_new, const void* v_n
  *           c = RNE(x * fp32(1 / s)), clamped; v_scale[pb][j][t] = s
  * k_new, v_new device bf16 [B][n_kv][d]. Descriptor: B, n_kv, d_h,
  * block_size, max_blocks_per_seq, num_blocks, kv_dtype = PDA_INT4; rows with
- * n <= 0 or n > max_blocks_per_seq * 16, or an unmapped block to encode,
- * append nothing. Errors: EINVAL, EHIP. */
+ * n <= 0 or n > max_blocks_per_seq * 16 append nothing; a block to encode
+ * that is unmapped (outside [0, num_blocks)) is skipped, the residual copy
+ * is still made. Errors: EINVAL, EHIP. */
 int32_t pda_kv_append_int4(const void* k_new, const void* v_new, const int32_t* block_table,
                            const int32_t* context_lens, void* k_q, void* v_q,
                            const float* k_scale, float* v_scale, void* k_res, void* v_res,
@@ -434,6 +435,22 @@ int32_t pda_paged_decode_attn_int4(const void* q, const void* k_q, const void* v
                                    const int32_t* block_table, const int32_t* context_lens,
                                    float scale, void* out, const pda_attn_desc* d,
                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* One fused decode step over that cache: the append of
+ * pda_kv_append_int4 and the attention of pda_paged_decode_attn_int4 in one
+ * call, with context_lens counting the new token. The waves that stream a
+ * row's blocks also do its append (the residual copy, and the encoding of a
+ * block the new token completes, before they read it), so the cache,
+ * v_scale, the residual buffers and out hold the same bits as the append
+ * followed by the attention. k_new, v_new device bf16 [B][n_kv][d]
+ * (new_dtype = PDA_BF16); every other argument, the workspace and the
+ * errors as for those two calls. */
+int32_t pda_decode_step_int4(const void* q, const void* k_new, const void* v_new, void* k_q,
+                             void* v_q, const float* k_scale, float* v_scale, void* k_res,
+                             void* v_res, const int32_t* block_table,
+                             const int32_t* context_lens, float scale, void* out,
+                             const pda_attn_desc* d, void* workspace, size_t ws_bytes,
+                             void* stream);
 
 /* Log-sum-exp merge of split-KV partial results. For each of `rows` rows and
  * P partials with (o_p, m_p, l_p):

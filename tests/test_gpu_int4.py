@@ -225,3 +225,83 @@ def test_int4_rejects_window_and_prefix():
         with pytest.raises(pda.PdaError):
             pda.paged_decode_attn_int4(t, t, t, t, t, t, t, t, t, 1.0, t, desc=desc,
                                        workspace=None)
+
+
+@pytest.mark.parametrize("d_h,n_q,n_kv,nw", [(128, 8, 2, 0), (128, 32, 8, 64), (64, 8, 2, 7),
+                                              (128, 8, 1, 1)])
+def test_int4_fused_step_matches_two_calls(d_h, n_q, n_kv, nw):
+    """decode_step_int4 against kv_append_int4 followed by
+    paged_decode_attn_int4, over 20 steps in which blocks fill at different
+    steps per row: outputs, codes, value scales and residual buffers
+    bit-identical after every step; the outputs also against the oracle at
+    the end. Rows include ones shorter than a block, an invalid length and a
+    row whose block to encode is unmapped (poisoned in both, append skipped)."""
+    import torch
+    import decode_attention_paged_slot_amd as pda
+    print(f"int4 fused step d_h={d_h} n_q={n_q} n_kv={n_kv} nw={nw}", flush=True)
+    steps = 20
+    start = np.array([1, 14, 15, 16, 31, 47, 5, 250, 511, 700, 3, 90], np.int32)
+    end = start + steps
+    st, ks, table, _, nb, mb = _case(5300 + d_h + nw, end, n_q=n_q, n_kv=n_kv, d_h=d_h,
+                                     poison=False)
+    bad_row, unmapped_row = 10, 11
+    table[unmapped_row, 5] = -1   # the block the token at n = 96 completes
+    r = np.random.default_rng(12 + nw)
+    dev = "cuda"
+    a_d, ks_d = _dev(st, ks, dev)
+    b_d, _ = _dev(st, ks, dev)
+    bt = torch.from_numpy(table).to(dev)
+
+    def bits(x):
+        return x.view(torch.int16 if x.element_size() == 2 else
+                      (torch.uint8 if x.element_size() == 1 else torch.int32)).cpu().numpy()
+
+    for k in range(steps):
+        ctx = start + k + 1
+        ctx[bad_row] = mb * 16 + 1
+        kn = to_dev(synth.gaussian((ctx.size, n_kv, d_h), BF16, r), BF16, dev)
+        vn = to_dev(synth.gaussian((ctx.size, n_kv, d_h), BF16, r), BF16, dev)
+        q_np = synth.gaussian((ctx.size, n_q, d_h), BF16, r)
+        q = to_dev(q_np, BF16, dev)
+        desc = _desc(ctx.size, n_q, n_kv, d_h, mb, nb, BF16, F32, ctx, nw)
+        ct = torch.from_numpy(ctx).to(dev)
+        out_a = torch.full((ctx.size, n_q, d_h), 7.0, device=dev)
+        out_b = torch.full((ctx.size, n_q, d_h), -7.0, device=dev)
+        pda.kv_append_int4(kn, vn, bt, ct, a_d["k"], a_d["v"], ks_d, a_d["v_scale"],
+                           a_d["k_res"], a_d["v_res"], desc=desc)
+        pda.paged_decode_attn_int4(q, a_d["k"], a_d["v"], ks_d, a_d["v_scale"], a_d["k_res"],
+                                   a_d["v_res"], bt, ct, 0.1, out_a, desc=desc,
+                                   workspace=pda.workspace_for(desc, dev))
+        pda.decode_step_int4(q, kn, vn, b_d["k"], b_d["v"], ks_d, b_d["v_scale"], b_d["k_res"],
+                             b_d["v_res"], bt, ct, 0.1, out_b, desc=desc,
+                             workspace=pda.workspace_for(desc, dev))
+        torch.cuda.synchronize()
+        assert (bits(out_a) == bits(out_b)).all(), f"output differs at step {k}"
+        for key in ("k", "v", "v_scale", "k_res", "v_res"):
+            assert (bits(a_d[key]) == bits(b_d[key])).all(), f"{key} differs at step {k}"
+        # the oracle follows the rows the kernels serve in full (the two
+        # poisoned rows are left out of it)
+        good = ctx.copy()
+        good[[bad_row, unmapped_row]] = 0
+        st = int4.kv_append_int4(st, kn.view(torch.int16).cpu().numpy().view(np.uint16),
+                                 vn.view(torch.int16).cpu().numpy().view(np.uint16), table,
+                                 good, ks)
+    got = out_b.cpu().numpy()
+    assert np.isnan(got[bad_row]).all() and np.isnan(got[unmapped_row]).all()
+    ref, _, _, _ = oracle.paged_attn_int4(q_np, st, ks, table, good, 0.1, n_q=n_q, n_kv=n_kv,
+                                          q_dtype=BF16)
+    ref = ref.reshape(got.shape)
+    for b in range(ctx.size):
+        if b not in (bad_row, unmapped_row):
+            assert_parity(float(np.abs(got[b] - ref[b]).max()), TOL_8BIT)
+
+
+def test_int4_fused_step_takes_bf16_rows_only():
+    import torch
+    import decode_attention_paged_slot_amd as pda
+    t = torch.zeros(4, device="cuda")
+    ctx = np.array([20], np.int32)
+    desc = _desc(1, 4, 2, 64, 2, 4, BF16, F32, ctx, 0)
+    desc.new_dtype = F32
+    with pytest.raises(ValueError):
+        pda.decode_step_int4(t, t, t, t, t, t, t, t, t, t, t, 1.0, t, desc=desc)
