@@ -299,12 +299,38 @@ ATTN_SOURCES = ("attn_mfma.hip", "attn_prefix.hip", "attn_f32.hip", "merge.hip",
                 "append_int4.hip", "device_common.h", "pda_internal.h", "api.cpp")
 
 
+def code_tokens(text: str) -> str:
+    """C / C++ source with comments removed and whitespace runs collapsed, so
+    that the hash below follows the code, not its comments or layout. String
+    and character literals are kept as written."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def attn_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for name in ATTN_SOURCES:
-        with open(os.path.join(ROOT, "decode_attention_paged_slot_amd", "csrc", name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(ROOT, "decode_attention_paged_slot_amd", "csrc", name)) as f:
+            h.update(name.encode() + b"\0" + code_tokens(f.read()).encode())
     return h.hexdigest()
 
 

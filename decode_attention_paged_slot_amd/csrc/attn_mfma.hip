@@ -1,5 +1,9 @@
 // attn_mfma.hip -- paged single-token decode attention on CDNA4 matrix cores,
-// for 16-bit (bf16) and 8-bit (fp8 e4m3 / int8 + per-block scale) caches.
+// for 16-bit (bf16) and 8-bit (fp8 e4m3 / int8 + per-block scale) caches, and
+// for 4-bit caches (codes with per-channel key scales and per-token value
+// scales; each row's open block stays in a bf16 residual window, read by the
+// merge; SoK paper section 2.3). With the step's new K/V rows (the fused
+// decode step), the waves that stream a row's blocks also append them.
 //
 // What is computed (sections 9.4-9.5 of "9 Decode and KV Cache"; SoK paper
 // section 1.1): for every sequence b, KV head j and the g = n_q / n_kv query
