@@ -497,6 +497,18 @@ def step_bytes_of(w, inp):
                           sinks=w.attn_sinks)
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def parity_and_cpu(w, inp, table, slots, shared, host, out, att_bytes):
     """Full-size parity of this run's output against the fp64 oracle, and the
     oracle's own rate on the host cores (the CPU baseline)."""
@@ -512,7 +524,7 @@ def parity_and_cpu(w, inp, table, slots, shared, host, out, att_bytes):
               "pass": bool(err < tol and info["bad_rows"] == 0 and info["tables_equal"]),
               "block_tables_identical": info["tables_equal"]}
     cpu = {"value": round(att_bytes / info["secs"] / 1e9, 4), "unit": "GB/s",
-           "cores": int(info["threads"]), "kind": "oracle",
+           "cores": int(info["threads"]), "kind": "oracle", "cpu_model": _cpu_model(),
            "sample": (f"whole workload {w.name} ({w.B} sequences x {w.n_q} query heads, "
                       f"{int(inp.ctx.sum())} cached tokens"
                       + (f", window {w.attn_window} + {w.attn_sinks} sinks"
