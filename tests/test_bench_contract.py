@@ -48,3 +48,14 @@ def test_committed_summaries_are_well_formed():
         assert len(fields["source_sha256"]) == 64, p
         workload = os.path.basename(p)[len("paged_decode_attn__"):-len("__pmc.txt")]
         assert os.path.exists(p.replace("__pmc.txt", "__kernel_trace.txt")), workload
+
+
+def test_source_hash_follows_code_not_comments():
+    a = 'int f(int x) { return x + 1; }  // add one\n/* block\n comment */ const char* s = "//x";\n'
+    b = '// a header\nint f(int x)   {\n    return x + 1;   /* same */ }\nconst char* s = "//x";\n'
+    c = 'int f(int x) { return x + 2; }\nconst char* s = "//x";\n'
+    d = 'int f(int x) { return x + 1; }\nconst char* s = "/x";\n'
+    assert bench.code_tokens(a) == bench.code_tokens(b)          # comments, layout
+    assert bench.code_tokens(a) != bench.code_tokens(c)          # code
+    assert bench.code_tokens(a) != bench.code_tokens(d)          # string literal contents
+    assert bench.code_tokens("char q = '\"'; // c") == "char q = '\"';"
