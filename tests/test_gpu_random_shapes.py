@@ -228,3 +228,69 @@ def test_random_int4_attention(i):
     empty = ctx == 0
     assert (got[empty] == 0).all()
     assert_parity(max_err(got[~empty], ref[~empty]), TOL_8BIT)
+
+
+N_INT4_STEP_CASES = 8
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_INT4_STEP_CASES))
+def test_random_int4_fused_step(i):
+    """The fused 4-bit decode step on random configurations (a third of the
+    rows complete a block this step): output, codes, value scales and
+    residual buffers bit for bit against the append followed by the
+    attention call, and the output against the oracle."""
+    import torch
+    import oracle
+    import synth
+    import decode_attention_paged_slot_amd as pda
+    from oracle import int4
+    from tests import test_gpu_int4 as i4
+    from tests.gpu_helpers import to_dev
+
+    d = _draw(5000 + i)
+    ctx = [(c + 15) // 16 * 16 if k % 3 == 0 and c > 0 else c for k, c in enumerate(d["ctx"])]
+    print(f"random fused 4-bit {i}: {d} lengths {ctx}", flush=True)
+    sys.stdout.flush()
+    n_q, n_kv, d_h = d["g"] * d["n_kv"], d["n_kv"], d["d_h"]
+    st, ks, table, ctx, nb, mb = i4._case(85_000 + i, ctx, n_q=n_q, n_kv=n_kv, d_h=d_h,
+                                          poison=False)
+    r = np.random.default_rng(86_000 + i)
+    dev = "cuda"
+    q_np = synth.gaussian((ctx.size, n_q, d_h), d["q_dtype"], r)
+    kn_np = synth.gaussian((ctx.size, n_kv, d_h), BF16, r)
+    vn_np = synth.gaussian((ctx.size, n_kv, d_h), BF16, r)
+    a_d, ks_d = i4._dev(st, ks, dev)
+    b_d, _ = i4._dev(st, ks, dev)
+    q = to_dev(q_np, d["q_dtype"], dev)
+    kn, vn = to_dev(kn_np, BF16, dev), to_dev(vn_np, BF16, dev)
+    bt, ct = torch.from_numpy(table).to(dev), torch.from_numpy(ctx).to(dev)
+    desc = i4._desc(ctx.size, n_q, n_kv, d_h, mb, nb, d["q_dtype"], F32, ctx, d["nw"])
+    scale = 1.0 / np.sqrt(d_h)
+    out_a = torch.full((ctx.size, n_q, d_h), 7.0, device=dev)
+    out_b = torch.full((ctx.size, n_q, d_h), -7.0, device=dev)
+    pda.kv_append_int4(kn, vn, bt, ct, a_d["k"], a_d["v"], ks_d, a_d["v_scale"], a_d["k_res"],
+                       a_d["v_res"], desc=desc)
+    pda.paged_decode_attn_int4(q, a_d["k"], a_d["v"], ks_d, a_d["v_scale"], a_d["k_res"],
+                               a_d["v_res"], bt, ct, scale, out_a, desc=desc,
+                               workspace=pda.workspace_for(desc, dev))
+    pda.decode_step_int4(q, kn, vn, b_d["k"], b_d["v"], ks_d, b_d["v_scale"], b_d["k_res"],
+                         b_d["v_res"], bt, ct, scale, out_b, desc=desc,
+                         workspace=pda.workspace_for(desc, dev))
+    torch.cuda.synchronize()
+
+    def bits(x):
+        return x.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[x.element_size()]).cpu().numpy()
+
+    assert (bits(out_a) == bits(out_b)).all()
+    for key in ("k", "v", "v_scale", "k_res", "v_res"):
+        assert (bits(a_d[key]) == bits(b_d[key])).all(), key
+    st = int4.kv_append_int4(st, kn_np, vn_np, table, ctx, ks)
+    ref, _, _, bad = oracle.paged_attn_int4(q_np, st, ks, table, ctx, scale, n_q=n_q, n_kv=n_kv,
+                                            q_dtype=d["q_dtype"])
+    assert bad == 0
+    got = out_b.cpu().numpy()
+    ref = ref.reshape(got.shape)
+    empty = ctx == 0
+    assert (got[empty] == 0).all()
+    assert_parity(max_err(got[~empty], ref[~empty]), TOL_8BIT)
