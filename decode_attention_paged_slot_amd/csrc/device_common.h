@@ -27,14 +27,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
-// Split x into bf16 hi (truncation) and bf16 lo (truncation of the exact
-// remainder): x - hi - lo is below 2^-16 |x|. Returns the two bf16 bit
-// patterns in the low halves.
+// Split x into bf16 hi (truncation) and bf16 lo (the exact remainder
+// rounded to nearest, ties away from zero): |x - hi - lo| <= 2^-16 |x|
+// (the remainder is below 2^-7 |x|, and rounding it to 8 significant bits
+// errs by at most half its last place). Truncating the remainder too would
+// allow twice that. Returns the two bf16 bit patterns in the low halves.
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
     const uint32_t u = __float_as_uint(x) & 0xFFFF0000u;
     const float r = x - __uint_as_float(u);       // exact
     hi = u >> 16;
-    lo = __float_as_uint(r) >> 16;
+    lo = (__float_as_uint(r) + 0x8000u) >> 16;    // the magnitude rounds; the sign bit stays
 }
 
 // fp32 -> OCP E4M3 code, round to nearest even with saturation to +-448.

@@ -12,6 +12,7 @@ exactly.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -21,7 +22,10 @@ from synth import F32, BF16, FP8, INT8
 from tests.helpers import make_case
 from tests.gpu_helpers import TOL_16BIT, TOL_8BIT, assert_parity, max_err, run_case
 
-N_CASES = 48
+# PDA_RANDOM_SCALE=k multiplies every case count below (a wider sweep of the
+# same seeded draws; the default run keeps k = 1)
+_K = max(1, int(os.environ.get("PDA_RANDOM_SCALE", "1")))
+N_CASES = 48 * _K
 
 
 def _draw(i: int) -> dict:
@@ -89,7 +93,7 @@ def test_random_configuration(i):
     assert_parity(max_err(got[keep], ref[keep]), tol)
 
 
-N_STEP_CASES = 16
+N_STEP_CASES = 16 * _K
 
 
 @pytest.mark.gpu
@@ -161,7 +165,7 @@ def test_random_fused_step(i):
     assert_parity(max_err(got[keep], ref[keep]), (TOL_8BIT if quant else TOL_16BIT))
 
 
-N_PREFIX_CASES = 16
+N_PREFIX_CASES = 16 * _K
 
 
 @pytest.mark.gpu
@@ -193,7 +197,7 @@ def test_random_shared_prefix(i):
     assert_parity(max_err(got, ref), tol)
 
 
-N_INT4_CASES = 12
+N_INT4_CASES = 12 * _K
 
 
 @pytest.mark.gpu
@@ -230,7 +234,7 @@ def test_random_int4_attention(i):
     assert_parity(max_err(got[~empty], ref[~empty]), TOL_8BIT)
 
 
-N_INT4_STEP_CASES = 8
+N_INT4_STEP_CASES = 8 * _K
 
 
 @pytest.mark.gpu
