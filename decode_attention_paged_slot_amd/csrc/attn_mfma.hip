@@ -95,6 +95,13 @@ __device__ __forceinline__ constexpr int dmap(int c, int grp) {
 
 __device__ __forceinline__ uint4 ld16(const char* p) { return *(const uint4*)p; }
 
+// global-address-space views, for loads whose base comes out of an asm
+// statement (a plain pointer there would be taken as a flat address)
+typedef __attribute__((address_space(1))) const char gchar;
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const u32x2 gu32x2;
+typedef __attribute__((address_space(1))) const f32x4 gf32x4;
+
 // Streaming 16-B load of cache data: a private K/V byte is read exactly once
 // per step, so the load is marked non-temporal and does not displace
 // reusable lines from the caches (measured on MI355X: random 4 KiB tile reads
@@ -496,6 +503,9 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                      ((blk < a.reuse_blocks) << 7) | (seg << 8);
             m.mask = pad ? 0 : (int)block_token_mask(blk, nn[b], a.window, a.sinks);
             if (QUANT && id >= 0) {
+                // ordinary loads: the n_kv heads of a block share these
+                // lines, so they are worth keeping in L2 (streaming them
+                // measured slower, unlike the 4-bit value scales below)
                 m.ksc = a.k_scale[m.tile];
                 m.vsc = a.v_scale[m.tile];
             }
@@ -506,11 +516,17 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     // ---- query operands (B operand of S^T = K . Q^T): lane (h, grp), for
     // the g query rows of segment `seg` (rows seg * g .. seg * g + g - 1)
     bf16x8 qhi[T::NCH], qlo[T::NCH];
-    // 4-bit: the per-channel key scales are folded into the queries,
-    // q' = q * k_scale[j][:] in fp32, split into bf16 hi + lo; the K operand
-    // holds 136 + code, so every score carries the offset 136 * sum_d q'_d,
-    // which cq removes (computed from the very hi and lo values multiplied)
+    // 4-bit: the per-channel key scales and the base-2 softmax scale are
+    // folded into the queries, q' = q * (k_scale[j][:] * scale_log2) in fp32,
+    // split into bf16 hi + lo; the K operand holds 136 + code, so every score
+    // carries the offset cq = 136 * sum_d q'_d (computed from the very hi and
+    // lo values multiplied). The score products start from -(cq + m_use4)
+    // (sinit), so they come out in the log2 domain relative to the piece's
+    // reference maximum, with no vector instruction per score.
     float cq = 0.0f;
+    float m_use4 = 0.0f;                  // the reference the 4-bit scores are relative to
+    float sinit = 0.0f;                   // -(cq + m_use4)
+    float thr4 = -__builtin_inff();       // rescale threshold: kSlack, or -inf before the first max
     auto load_q = [&](int seg) {
         const bool live = col < g;
         const int64_t qrow = ((int64_t)seg * g + (live ? col : 0)) * HD;
@@ -538,8 +554,9 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                     const float* ks = a.k_scale + (int64_t)(seg % n_kv) * HD + d0;
                     const float4 k0 = *(const float4*)ks;
                     const float4 k1 = *(const float4*)(ks + 4);
-                    f[0] *= k0.x; f[1] *= k0.y; f[2] *= k0.z; f[3] *= k0.w;
-                    f[4] *= k1.x; f[5] *= k1.y; f[6] *= k1.z; f[7] *= k1.w;
+                    const float sl = a.scale_log2;
+                    f[0] *= k0.x * sl; f[1] *= k0.y * sl; f[2] *= k0.z * sl; f[3] *= k0.w * sl;
+                    f[4] *= k1.x * sl; f[5] *= k1.y * sl; f[6] *= k1.z * sl; f[7] *= k1.w * sl;
                 }
                 uint32_t h16[8], l16[8];
 #pragma unroll
@@ -576,7 +593,10 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 qlo[c] = __builtin_bit_cast(bf16x8, lv);
             }
         }
-        if constexpr (I4) cq = kInt4Bias * sum_rows4(part);
+        if constexpr (I4) {
+            cq = kInt4Bias * sum_rows4(part);
+            sinit = -(cq + m_use4);
+        }
     };
 
     // ---- per-piece online-softmax state
@@ -676,6 +696,8 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     // unmapped entry loads block 0 and poisons its piece), so every refill
     // issues the same instructions and the waits before each block's math
     // only drain that block's loads.
+    // 4-bit loads: this lane's byte offset in a tile and in its value scales
+    uint32_t i4_off = col * T::ROWB + grp * T::LB, i4_soff = 16u * (uint32_t)grp;
     auto issue = [&](int s, int i) {
         // the (block, head) tile: its index comes with the block's metadata,
         // so no division by n_kv happens per block
@@ -691,17 +713,35 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             // holding channels (d_h / 4) grp .. +d_h / 4, for K (straight
             // into the operand) and V (through LDS) alike, and the value
             // scales of its tokens 4 grp .. 4 grp + 3
-            const int off = col * T::ROWB + grp * T::LB;
+            // The tile bases are wave-uniform; the empty asm pins them in
+            // scalar registers, so each load takes base + the lane's 32-bit
+            // offset and no 64-bit vector address is formed per load.
+            // The lane offsets are redefined in place by the same asm, so
+            // their zero extension is formed beside the loads rather than
+            // hoisted, which is what lets the loads take that form.
+            uint64_t kb = (uint64_t)kt, vb = (uint64_t)vt, sb = (uint64_t)(a.v_scale + tile * 16);
+            asm volatile("" : "+s"(kb), "+s"(vb), "+s"(sb), "+v"(i4_off), "+v"(i4_soff));
+            const uint32_t off = i4_off, soff = i4_soff;
+            const gchar* kg = (const gchar*)kb;
+            const gchar* vg = (const gchar*)vb;
+            const gchar* sg = (const gchar*)sb;
             if constexpr (T::LB == 16) {
-                kr[s][0] = ld16_stream(kt + off);
-                vr[s][0] = ld16_stream(vt + off);
+                const u32x4 kk = __builtin_nontemporal_load((const gu32x4*)(kg + off));
+                const u32x4 vv = __builtin_nontemporal_load((const gu32x4*)(vg + off));
+                kr[s][0] = make_uint4(kk.x, kk.y, kk.z, kk.w);
+                vr[s][0] = make_uint4(vv.x, vv.y, vv.z, vv.w);
             } else {
-                const u32x2 kk = __builtin_nontemporal_load((const u32x2*)(kt + off));
-                const u32x2 vv = __builtin_nontemporal_load((const u32x2*)(vt + off));
+                const u32x2 kk = __builtin_nontemporal_load((const gu32x2*)(kg + off));
+                const u32x2 vv = __builtin_nontemporal_load((const gu32x2*)(vg + off));
                 kr[s][0] = make_uint4(kk.x, kk.y, 0, 0);
                 vr[s][0] = make_uint4(vv.x, vv.y, 0, 0);
             }
-            vsr[s] = *(const f32x4*)(a.v_scale + tile * 16 + 4 * grp);
+            // the value scales are streamed like the codes (only this wave
+            // reads a tile's): as an ordinary load, this one made the
+            // 70B-shape 4-bit step 10 us slower when it ran right after a
+            // 1 GiB write, i.e. with the caches full of dirty lines (MI355X:
+            // 82.7 against 72.7 us)
+            vsr[s] = __builtin_nontemporal_load((const gf32x4*)(sg + soff));
             return;
         }
         const int koff = KST ? 16 * lane : col * T::ROWB + 16 * grp;
@@ -764,6 +804,11 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         m_run = -__builtin_inff();
         l_run = 0.0f;
         wfed = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (I4) {
+            m_use4 = 0.0f;
+            sinit = -cq;
+            thr4 = -__builtin_inff();
+        }
 #pragma unroll
         for (int t = 0; t < T::NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
         piece_bad = false;
@@ -817,6 +862,28 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         }
         const u32x4 pb4 = {H[0], H[1], L[0], L[1]};
         return __builtin_bit_cast(bf16x8, pb4);
+    };
+
+    // 4-bit: the scores come out relative to m_use4. When some head's
+    // maximum exceeds its reference by more than kSlack (the test against
+    // thr4), the reference moves as in the other caches, and this step's
+    // scores are shifted to the new one.
+    auto rescale4 = [&](float lmx, auto& sv) {
+        const float mx = max_rows4(lmx) + m_use4;
+        const float m_new = mx > m_run + kSlack ? mx : m_run;
+        const float alpha = m_run == -__builtin_inff() ? 0.0f
+                                                       : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        wfed *= alpha;
+#pragma unroll
+        for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
+        m_run = m_new;
+        const float mu = m_run == -__builtin_inff() ? 0.0f : m_run;
+        const float d = m_use4 - mu;
+        for (auto& x : sv) x += d;
+        m_use4 = mu;
+        sinit = -(cq + mu);
+        thr4 = m_run == -__builtin_inff() ? -__builtin_inff() : kSlack;
     };
 
     auto consume = [&](int s, int i, bool refill) {
@@ -934,9 +1001,11 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 *(uint4*)(kstage + vrow[l] * T::ROWB +
                           16 * ((lane % T::CPRB) ^ kswz<HD>(vrow[l]))) = kr[s][l];
         }
-        // scores S^T = K . Q^T; with a hi + lo query the two passes go to
-        // separate accumulators, two independent chains of matrix products
+        // scores S^T = K . Q^T; with an fp32 query the hi and lo passes go
+        // to separate accumulators, two independent chains of matrix
+        // products (4-bit: one chain from sinit, in the log2 domain)
         f32x4 st = {0, 0, 0, 0}, stl = {0, 0, 0, 0};
+        if constexpr (I4) st = f32x4{sinit, sinit, sinit, sinit};
 #pragma unroll
         for (int c = 0; c < T::NCH; ++c) {
             bf16x8 kop;
@@ -949,10 +1018,12 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                 kop = kv_operand_from_bytes<KV>(kr[s][c / 2], c % 2);
             }
             st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qhi[c], st, 0, 0, 0);
-            if (QT == DT_F32 || I4)
+            if constexpr (I4)
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], st, 0, 0, 0);
+            else if (QT == DT_F32)
                 stl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qlo[c], stl, 0, 0, 0);
         }
-        if (QT == DT_F32 || I4) st += stl;
+        if (QT == DT_F32 && !I4) st += stl;
         // refill this slot with the block kDepth ahead
         if (refill) issue(s, i + kDepth);
 
@@ -960,7 +1031,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         const float mult = a.scale_log2 * ksc;
         float sv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[e] = (I4 ? st[e] - cq : st[e]) * mult;
+        for (int e = 0; e < 4; ++e) sv[e] = I4 ? st[e] : st[e] * mult;
         if (mask != 0xFFFFu) {   // wave-uniform: a partial or windowed block
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -973,7 +1044,9 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         // the rare blocks where some head's max jumps (the first block of a
         // piece always sets it). Any reference gives the same softmax: the
         // partial carries (reference, sum) together.
-        if (__builtin_amdgcn_ballot_w64(lmx > m_run + kSlack) != 0) {
+        if (I4 && __builtin_amdgcn_ballot_w64(lmx > thr4) != 0) {
+            rescale4(lmx, sv);
+        } else if (!I4 && __builtin_amdgcn_ballot_w64(lmx > m_run + kSlack) != 0) {
             // some head's block max exceeds its reference by more than the
             // slack (a head's max exceeds iff one of its four lanes' does):
             // only then is the cross-lane max of each head formed
@@ -982,12 +1055,11 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             const float alpha = m_run == -__builtin_inff() ? 0.0f
                                                            : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
-            if (I4) wfed *= alpha;
 #pragma unroll
             for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
             m_run = m_new;
         }
-        const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+        const float m_use = (I4 || m_run == -__builtin_inff()) ? 0.0f : m_run;
         float pe[4], psum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1057,8 +1129,8 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             }
         }
         // scores of both blocks: two independent chains (the hi and lo
-        // query passes of each block accumulate together)
-        f32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+        // query passes of each block accumulate together, from sinit)
+        f32x4 s0 = {sinit, sinit, sinit, sinit}, s1 = s0;
         {
             const uint32_t k0[4] = {kr[s][0].x, kr[s][0].y, kr[s][0].z, kr[s][0].w};
             const uint32_t k1[4] = {kr[s + 1][0].x, kr[s + 1][0].y, kr[s + 1][0].z,
@@ -1076,35 +1148,27 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         issue(s, i + kDepth);
         issue(s + 1, i + 1 + kDepth);
 
-        // online softmax over the step's 32 tokens (base-2 domain)
-        const float mult = a.scale_log2;
+        // online softmax over the step's 32 tokens (base-2 domain, relative
+        // to m_use4)
         float sv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sv[e] = (s0[e] - cq) * mult;
-            sv[4 + e] = mask1 != 0 ? (s1[e] - cq) * mult : -__builtin_inff();
+            sv[e] = s0[e];
+            sv[4 + e] = mask1 != 0 ? s1[e] : -__builtin_inff();
         }
-        const float lmx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                                fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        if (__builtin_amdgcn_ballot_w64(lmx > m_run + kSlack) != 0) {   // as in consume
-            const float mx = max_rows4(lmx);
-            const float m_new = mx > m_run + kSlack ? mx : m_run;
-            const float alpha = m_run == -__builtin_inff() ? 0.0f
-                                                           : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-            wfed *= alpha;
+        // the NaN-propagating maximum takes matrix-product results as they
+        // are (fmaxf would first quiet each one with an extra instruction);
+        // a NaN score (from a NaN query) makes the output NaN either way
+        auto mx3 = [](float x, float y, float z) {
+            return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+        };
+        const float lmx = mx3(mx3(sv[0], sv[1], sv[2]), mx3(sv[3], sv[4], sv[5]),
+                              __builtin_elementwise_maximum(sv[6], sv[7]));
+        if (__builtin_amdgcn_ballot_w64(lmx > thr4) != 0) rescale4(lmx, sv);
+        float pe[8];
 #pragma unroll
-            for (int t = 0; t < T::NT; ++t) acc[t] *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
-        float pe[8], psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
-            psum += pe[e];
-        }
-        l_run += psum;
+        for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e]);
+        l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
         float w0[4], w1[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1117,20 +1181,21 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
                                                        0, 0, 0);
         wfed = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), p1, wfed,
                                                        0, 0, 0);
-        // O^T += [V0^T | V0^T] . [P0_hi ; P0_lo] + [V1^T | V1^T] . [P1_hi ; P1_lo]
+        // O^T += [V0^T | V0^T] . [P0_hi ; P0_lo] + [V1^T | V1^T] . [P1_hi ; P1_lo].
+        // The empty asm redefines each address register in place once per
+        // step, so the second tile's address (kStage2 past the first) cannot
+        // be hoisted into registers of its own and is folded into the read's
+        // offset instead.
+#pragma unroll
+        for (int t = 0; t < T::NT; ++t) asm volatile("" : "+v"(trd0[t]), "+v"(trd1[t]));
 #pragma unroll
         for (int t = 0; t < T::NT; ++t) {
             const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)trd0[t]);
             const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)trd1[t]);
-            // the second tile's addresses: kStage2 past the first (added at
-            // the read, where it becomes the instruction's offset, so no
-            // second set of address registers stays live)
-            uint32_t ab0 = trd0[t], ab1 = trd1[t];
-            asm volatile("" : "+v"(ab0), "+v"(ab1));
             const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(uintptr_t)(ab0 + kStage2));
+                (lds_s16x4*)(uintptr_t)(trd0[t] + kStage2));
             const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(uintptr_t)(ab1 + kStage2));
+                (lds_s16x4*)(uintptr_t)(trd1[t] + kStage2));
             const s16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             const s16x8 vb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), p0,
