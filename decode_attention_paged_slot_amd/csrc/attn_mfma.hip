@@ -848,11 +848,9 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     // [H2 H3], [L0 L1], [L2 L3]: a permlane32 swap of (H, L) then a
     // permlane16 swap regroups them.
     auto pack_p = [&](const float (&w)[4]) -> bf16x8 {
-        uint32_t hi16[4], lo16[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_bf16(w[e], hi16[e], lo16[e]);
-        uint32_t H[2] = {hi16[0] | (hi16[1] << 16), hi16[2] | (hi16[3] << 16)};
-        uint32_t L[2] = {lo16[0] | (lo16[1] << 16), lo16[2] | (lo16[3] << 16)};
+        uint32_t H[2], L[2];
+        split_bf16x2(w[0], w[1], H[0], L[0]);
+        split_bf16x2(w[2], w[3], H[1], L[1]);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const auto x = __builtin_amdgcn_permlane32_swap(H[q], L[q], false, false);

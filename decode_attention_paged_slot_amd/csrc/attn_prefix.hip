@@ -233,11 +233,9 @@ __global__ void __launch_bounds__(kPrefixThreads) k_attn_prefix(AttnArgs a, int3
     };
     // P split into bf16 hi + lo and regrouped into the packed B operand
     auto p_operand = [&](const float* pe, float vsc) {
-        uint32_t hi16[4], lo16[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_bf16(pe[e] * vsc, hi16[e], lo16[e]);
-        uint32_t H[2] = {hi16[0] | (hi16[1] << 16), hi16[2] | (hi16[3] << 16)};
-        uint32_t Lw[2] = {lo16[0] | (lo16[1] << 16), lo16[2] | (lo16[3] << 16)};
+        uint32_t H[2], Lw[2];
+        split_bf16x2(pe[0] * vsc, pe[1] * vsc, H[0], Lw[0]);
+        split_bf16x2(pe[2] * vsc, pe[3] * vsc, H[1], Lw[1]);
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
             const auto x = __builtin_amdgcn_permlane32_swap(H[w], Lw[w], false, false);

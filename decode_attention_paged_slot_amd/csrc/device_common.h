@@ -39,6 +39,20 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
     lo = (__float_as_uint(r) + 0x8000u) >> 16;    // the magnitude rounds; the sign bit stays
 }
 
+// Two values at once, with the gfx950 packed conversion: hi = bf16 RNE of x,
+// lo = bf16 RNE of the exact remainder x - hi; the same bound,
+// |x - hi - lo| <= 2^-16 |x| (the remainder is at most 2^-8 |x| and its
+// rounding errs by at most 2^-8 of it). Returns the packed pairs (x0 in the
+// low half).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const f32x2 x = {x0, x1};
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    const f32x2 r = {x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
+
 // fp32 -> OCP E4M3 code, round to nearest even with saturation to +-448.
 // NaN -> 0x7F; the sign of y is kept (so -0 -> 0x80).
 __device__ __forceinline__ uint32_t quant_fp8_e4m3(float y) {
