@@ -238,9 +238,11 @@ def read_probe(dev, table, ctx, w, reps=10):
     """Read-only HBM probes (pda_hbm_read_probe), GB/s: a sequential walk of
     2 GiB (2048 waves), and the (block, head) K and V tiles of this workload
     read in the attention kernel's order (segment by segment, K then V per
-    block, 1024 waves, four tiles in flight), from a buffer laid out like the
-    two caches. Each figure is the median of 5 runs of `reps` back-to-back
-    launches between two HIP events."""
+    block, four tiles in flight, with the kernel's wave count: 1024 for bf16
+    caches, 2048 for 8-bit and 4-bit ones), from a buffer laid out like the
+    two caches (the 4-bit value scales are not read). Each figure is the
+    median of 5 runs of `reps` back-to-back launches between two HIP
+    events."""
     import torch
     import synth
     import decode_attention_paged_slot_amd as pda
@@ -267,8 +269,9 @@ def read_probe(dev, table, ctx, w, reps=10):
     ms = timed(pda.hbm_read_probe(buf, sink, waves=2048, bind=True))
     out["sequential_GBps"] = round(seq_bytes / (ms * 1e-3) / 1e9, 1)
     del buf
-    if w.kv_dtype in (synth.BF16, synth.FP8, synth.INT8) and not w.attn_window:
+    if w.kv_dtype in (synth.BF16, synth.FP8, synth.INT8, synth.INT4) and not w.attn_window:
         eb = synth.ELEM_BYTES[w.kv_dtype]
+        waves = 1024 if w.kv_dtype == synth.BF16 else 2048
         tile = int(16 * w.d_h * eb)                    # one (block, head) tile
         blk = w.n_kv * tile                            # one physical block, all heads
         nblk = synth.blocks_needed(ctx, w.block_size)
@@ -282,8 +285,8 @@ def read_probe(dev, table, ctx, w, reps=10):
         offs = np.concatenate(offs)
         buf = torch.empty(2 * nb_pool * blk // 4, dtype=torch.int32, device=dev).fill_(1)
         t_off = torch.from_numpy(offs).to(dev)
-        sink = torch.empty(1024 * 64, dtype=torch.int32, device=dev)
-        ms = timed(pda.hbm_read_probe(buf, sink, tile_offsets=t_off, tile_bytes=tile, waves=1024,
+        sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+        ms = timed(pda.hbm_read_probe(buf, sink, tile_offsets=t_off, tile_bytes=tile, waves=waves,
                                       bind=True))
         out["kv_tiles_GBps"] = round(offs.size * tile / (ms * 1e-3) / 1e9, 1)
         out["kv_tiles_us"] = round(ms * 1e3, 2)
