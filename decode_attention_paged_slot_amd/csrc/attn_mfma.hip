@@ -153,7 +153,9 @@ __device__ __forceinline__ uint32_t encode_lane(uint2 w, int src_dtype, float in
 // the row, or its sink and window blocks with a sliding window).
 struct Meta {
     int id;      // physical block, or -1 when the table entry is unmapped
-    int tile;    // (block, head) tile index id * n_kv + j (block 0 when unmapped)
+                 // (bf16: the raw table entry, checked where used)
+    int tile;    // (block, head) tile index id * n_kv + j (block 0 when
+                 // unmapped); bf16: the head j
     int info;
     int mask;    // attended positions of the block (bit k: token k)
     float ksc, vsc;
@@ -164,6 +166,11 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     constexpr int kDepth = KV == DT_INT4 ? kDepthInt4 : pda::kDepth;   // this kernel's depth
     using T = Tr<HD, KV>;
     constexpr bool QUANT = KV == DT_FP8 || KV == DT_INT8;   // 8-bit, per-(block, head) scales
+    // bf16: block metadata keeps the raw table entry and the head rather
+    // than the checked id and tile index (8-bit caches need the tile there
+    // for their scale loads; loading the scales with each block's tiles
+    // instead made the 8-bit calls 30% slower)
+    constexpr bool kLazyId = KV == DT_BF16;
     constexpr bool I4 = KV == DT_INT4;   // 4-bit: per-channel K and per-token V scales
     // per wave: the V tile (bf16) and, for bf16 caches, the K tile
     constexpr bool KST = KV == DT_BF16;
@@ -176,6 +183,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     int* pre = dyn_lds;             // [B + 1] exclusive prefix of blocks per sequence
     int* nn = dyn_lds + a.B + 1;    // [B] context length, -1 for an invalid one
     int* preu = dyn_lds + 2 * a.B + 1;   // [B + 1] exclusive prefix of split units per sequence
+    int* plen = dyn_lds + 3 * a.B + 2;   // [B] shared-prefix lengths as given (prefix calls)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -212,6 +220,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             if (b < B) {
                 const int n = a.context_lens[b];
                 const int c = seg_blocks(b, n);
+                if (a.prefix_lens != nullptr) plen[b] = a.prefix_lens[b];
                 nn[b] = c < 0 ? -1 : n;
                 const int cb = max(c, 0);
                 local += cb;
@@ -486,16 +495,26 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             const int bl = r0 - j * nb;   // attended-block index within the row
             // rows with a shared prefix: their first pl blocks belong to the
             // prefix pass, this pass starts after them (no window there)
-            const int pl = a.prefix_lens == nullptr ? 0 : a.prefix_lens[b];
+            // (from LDS: a global load here would be waited for, with every
+            // load issued before it, before the block lookup goes out)
+            const int pl = a.prefix_lens == nullptr ? 0 : plen[b];
             const int blk = row_block_logical(row_blocks(nn[b], a.window, a.sinks), bl) + pl;
             // 4-bit: the pad block that evens a segment's block count is
             // fully masked and reads block 0 (no table lookup, no poison)
             const bool pad = I4 && bl >= (nn[b] >> 4);
             int id = pad ? 0 : a.block_table[(int64_t)b * a.max_blocks + blk];
-            if (id < 0 || id >= a.num_blocks) id = -1;
             const int seg = b * n_kv + j;
-            m.id = id;
-            m.tile = (id < 0 ? 0 : id) * n_kv + j;
+            if constexpr (kLazyId) {
+                // the id is range-checked where it is used (issue, consume),
+                // so nothing here waits for the table load and a second
+                // batch's lookups are in flight with the first's
+                m.id = id;
+                m.tile = j;
+            } else {
+                if (id < 0 || id >= a.num_blocks) id = -1;
+                m.id = id;
+                m.tile = (id < 0 ? 0 : id) * n_kv + j;
+            }
             // bit 4: the row's pieces always go to the merge (a shared
             // prefix, or a 4-bit cache's non-empty residual window)
             const bool merged = pl > 0 || (a.extra_pieces > 0 && (nn[b] & 15) != 0);
@@ -662,27 +681,30 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     };
     auto meta_tile = [&](int i) {
         const int v = (i >> 6) == batchA ? A.tile : Bm.tile;
-        return __builtin_amdgcn_readlane(v, i & 63);
+        const int t = __builtin_amdgcn_readlane(v, i & 63);
+        if constexpr (kLazyId) {
+            const int vi = (i >> 6) == batchA ? A.id : Bm.id;
+            const int id = __builtin_amdgcn_readlane(vi, i & 63);
+            return ((unsigned)id < (unsigned)a.num_blocks ? id : 0) * n_kv + t;
+        }
+        return t;
     };
     auto meta_mask = [&](int i) {
         const int v = (i >> 6) == batchA ? A.mask : Bm.mask;
         return (uint32_t)__builtin_amdgcn_readlane(v, i & 63);
     };
-    auto meta_f = [&](float fa, float fb, int i) {
-        const float v = (i >> 6) == batchA ? fa : fb;
-        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i & 63));
-    };
 
-    auto ksc_of = [&](int i) { return QUANT ? meta_f(A.ksc, Bm.ksc, i) : 1.0f; };
-    auto vsc_of = [&](int i) { return QUANT ? meta_f(A.vsc, Bm.vsc, i) : 1.0f; };
     // the consumed block always lies in batch A (the consumer moves to the
     // next batch first), so its fields need no batch select
-    auto cur_id = [&](int i) { return __builtin_amdgcn_readlane(A.id, i & 63); };
+    auto cur_id = [&](int i) {
+        const int id = __builtin_amdgcn_readlane(A.id, i & 63);
+        return (!kLazyId || (unsigned)id < (unsigned)a.num_blocks) ? id : -1;
+    };
     auto cur_info = [&](int i) { return __builtin_amdgcn_readlane(A.info, i & 63); };
-    auto cur_mask = [&](int i) { return (uint32_t)__builtin_amdgcn_readlane(A.mask, i & 63); };
     auto cur_f = [&](float f, int i) {
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), i & 63));
     };
+    auto cur_mask = [&](int i) { return (uint32_t)__builtin_amdgcn_readlane(A.mask, i & 63); };
 
     uint4 kr[kDepth][T::LOADS], vr[kDepth][T::LOADS];
     f32x4 vsr[kDepth];   // 4-bit: value scales of this lane's 4 tokens
@@ -1242,7 +1264,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 
 }  // namespace
 
-size_t attn_mfma_dyn_lds(int32_t B) { return (size_t)(3 * B + 2) * sizeof(int32_t); }
+size_t attn_mfma_dyn_lds(int32_t B) { return (size_t)(4 * B + 2) * sizeof(int32_t); }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
     const int waves = a.split ? a.nw : a.B * a.n_kv;
