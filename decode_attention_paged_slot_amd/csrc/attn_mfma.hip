@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     int* pre = dyn_lds;             // [B + 1] exclusive prefix of blocks per sequence
     int* nn = dyn_lds + a.B + 1;    // [B] context length, -1 for an invalid one
     int* preu = dyn_lds + 2 * a.B + 1;   // [B + 1] exclusive prefix of split units per sequence
-    int* plen = dyn_lds + 3 * a.B + 2;   // [B] shared-prefix lengths as given (prefix calls)
+    int* plen = dyn_lds + 3 * a.B + 2;   // [B] shared-prefix lengths as given (prefix calls only)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -1264,13 +1264,16 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 
 }  // namespace
 
-size_t attn_mfma_dyn_lds(int32_t B) { return (size_t)(4 * B + 2) * sizeof(int32_t); }
+// pre, nn and preu, plus the prefix lengths for the shared-prefix calls
+size_t attn_mfma_dyn_lds(int32_t B, bool prefix) {
+    return (size_t)((prefix ? 4 : 3) * B + 2) * sizeof(int32_t);
+}
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
     const int waves = a.split ? a.nw : a.B * a.n_kv;
     dim3 grid((waves + 3) / 4);
     dim3 block(kAttnThreads);
-    const size_t lds = attn_mfma_dyn_lds(a.B);
+    const size_t lds = attn_mfma_dyn_lds(a.B, a.prefix_lens != nullptr);
 #define PDA_LAUNCH(HD, KV, QT) \
     hipLaunchKernelGGL((k_attn_mfma<HD, KV, QT>), grid, block, lds, s, a)
 #define PDA_BY_Q(HD, KV)                          \

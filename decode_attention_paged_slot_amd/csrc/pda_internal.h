@@ -96,7 +96,7 @@ hipError_t launch_append_int4(const void* k_new, const void* v_new, const int32_
                               int32_t num_blocks, hipStream_t s);
 hipError_t launch_merge_for_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge_stream(const AttnArgs& a, hipStream_t s);
-size_t attn_mfma_dyn_lds(int32_t B);
+size_t attn_mfma_dyn_lds(int32_t B, bool prefix);
 hipError_t launch_read_probe(const void* buf, size_t bytes, const int64_t* tile_offsets,
                              int64_t n_tiles, int32_t tile_bytes, int32_t waves,
                              uint32_t* sink, hipStream_t s);
