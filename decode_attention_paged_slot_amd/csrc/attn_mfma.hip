@@ -546,7 +546,36 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     float m_use4 = 0.0f;                  // the reference the 4-bit scores are relative to
     float sinit = 0.0f;                   // -(cq + m_use4)
     float thr4 = -__builtin_inff();       // rescale threshold: kSlack, or -inf before the first max
-    auto load_q = [&](int seg) {
+    // 4-bit: a segment's query words and key scales, fetched (q_fetch) and
+    // then combined (q_finish) in two steps, so that the first segment's
+    // fetch is in flight together with the first tiles while its arithmetic
+    // waits only for itself
+    float4 qw[T::NCH][2], kw4[T::NCH][2];
+    auto q_fetch = [&](int seg) {
+        if constexpr (I4) {
+            const bool live = col < g;
+            const int64_t qrow = ((int64_t)seg * g + (live ? col : 0)) * HD;
+#pragma unroll
+            for (int c = 0; c < T::NCH; ++c) {
+                const int d0 = dmap<HD, KV>(c, grp);
+                if (QT == DT_BF16) {
+                    const uint4 w = live ? ld16((const char*)a.q + (qrow + d0) * 2)
+                                         : make_uint4(0, 0, 0, 0);
+                    qw[c][0] = __builtin_bit_cast(float4, w);
+                } else {
+                    qw[c][0] = live ? *(const float4*)((const float*)a.q + qrow + d0)
+                                    : make_float4(0, 0, 0, 0);
+                    qw[c][1] = live ? *(const float4*)((const float*)a.q + qrow + d0 + 4)
+                                    : make_float4(0, 0, 0, 0);
+                }
+                const float* ks = a.k_scale + (int64_t)(seg % n_kv) * HD + d0;
+                kw4[c][0] = *(const float4*)ks;
+                kw4[c][1] = *(const float4*)(ks + 4);
+            }
+        }
+    };
+    auto load_q = [&](int seg, bool fetched = false) {
+        if (I4 && !fetched) q_fetch(seg);
         const bool live = col < g;
         const int64_t qrow = ((int64_t)seg * g + (live ? col : 0)) * HD;
         float part = 0.0f;
@@ -554,29 +583,23 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         for (int c = 0; c < T::NCH; ++c) {
             const int d0 = dmap<HD, KV>(c, grp);
             if constexpr (I4) {
-                float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (live) {
-                    if (QT == DT_BF16) {
-                        const uint4 w = ld16((const char*)a.q + (qrow + d0) * 2);
-                        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+                float f[8];
+                if (QT == DT_BF16) {
+                    const uint4 w = __builtin_bit_cast(uint4, qw[c][0]);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            f[2 * k] = bf16_lo_to_f32(ws[k]);
-                            f[2 * k + 1] = bf16_hi_to_f32(ws[k]);
-                        }
-                    } else {
-                        const float4 x0 = *(const float4*)((const float*)a.q + qrow + d0);
-                        const float4 x1 = *(const float4*)((const float*)a.q + qrow + d0 + 4);
-                        f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
-                        f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+                    for (int k = 0; k < 4; ++k) {
+                        f[2 * k] = bf16_lo_to_f32(ws[k]);
+                        f[2 * k + 1] = bf16_hi_to_f32(ws[k]);
                     }
-                    const float* ks = a.k_scale + (int64_t)(seg % n_kv) * HD + d0;
-                    const float4 k0 = *(const float4*)ks;
-                    const float4 k1 = *(const float4*)(ks + 4);
-                    const float sl = a.scale_log2;
-                    f[0] *= k0.x * sl; f[1] *= k0.y * sl; f[2] *= k0.z * sl; f[3] *= k0.w * sl;
-                    f[4] *= k1.x * sl; f[5] *= k1.y * sl; f[6] *= k1.z * sl; f[7] *= k1.w * sl;
+                } else {
+                    f[0] = qw[c][0].x; f[1] = qw[c][0].y; f[2] = qw[c][0].z; f[3] = qw[c][0].w;
+                    f[4] = qw[c][1].x; f[5] = qw[c][1].y; f[6] = qw[c][1].z; f[7] = qw[c][1].w;
                 }
+                const float4 k0 = kw4[c][0], k1 = kw4[c][1];
+                const float sl = a.scale_log2;
+                f[0] *= k0.x * sl; f[1] *= k0.y * sl; f[2] *= k0.z * sl; f[3] *= k0.w * sl;
+                f[4] *= k1.x * sl; f[5] *= k1.y * sl; f[6] *= k1.z * sl; f[7] *= k1.w * sl;
                 uint32_t h16[8], l16[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -1227,9 +1250,12 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             flush(seg, piece_whole && seg_last && !((info1 >> 4) & 1));
     };
 
-    // the first segment's queries, in flight with the first tiles
+    // the first segment's queries, in flight with the first tiles (4-bit:
+    // fetched before them, combined after them)
     q_seg = (int)((unsigned)meta_info(0) >> 8);
-    load_q(q_seg);
+    if constexpr (I4) q_fetch(q_seg);
+    else load_q(q_seg);
+    __builtin_amdgcn_sched_barrier(0);
     int it = 0;
     if (cnt >= 2 * kDepth) {
         // prologue and steady state issue unconditionally and in slot order
@@ -1241,6 +1267,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
             issue(s, s);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (I4) load_q(q_seg, true);
         for (; it + 2 * kDepth <= cnt; it += kDepth) {
             if constexpr (I4) {
                 static_assert(kDepth % 2 == 0, "4-bit steps take blocks in pairs");
@@ -1255,6 +1282,7 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
 #pragma unroll
         for (int s = 0; s < kDepth; ++s)
             if (s < cnt) issue(s, s);
+        if constexpr (I4) load_q(q_seg, true);
     }
     // drain: fewer than 2 * kDepth blocks remain, their first loads issued
 #pragma unroll
