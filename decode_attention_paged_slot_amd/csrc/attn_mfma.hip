@@ -546,10 +546,10 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
     float m_use4 = 0.0f;                  // the reference the 4-bit scores are relative to
     float sinit = 0.0f;                   // -(cq + m_use4)
     float thr4 = -__builtin_inff();       // rescale threshold: kSlack, or -inf before the first max
-    // 4-bit: a segment's query words and key scales, fetched (q_fetch) and
-    // then combined (q_finish) in two steps, so that the first segment's
-    // fetch is in flight together with the first tiles while its arithmetic
-    // waits only for itself
+    // 4-bit: a segment's query words and key scales are fetched (q_fetch)
+    // and then combined (load_q with fetched = true) in two steps, so that
+    // the first segment's fetch is in flight together with the first tiles
+    // while its arithmetic waits only for itself
     float4 qw[T::NCH][2], kw4[T::NCH][2];
     auto q_fetch = [&](int seg) {
         if constexpr (I4) {
