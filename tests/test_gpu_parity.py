@@ -240,6 +240,22 @@ def test_unmapped_block_poisons_only_its_row(parts):
     assert_parity(max_err(got[[0, 1]], ref[[0, 1]]), TOL_16BIT)
 
 
+@pytest.mark.parametrize("bad_id", [-1, 1 << 20])
+@pytest.mark.parametrize("kv", [BF16, FP8])
+def test_bad_block_in_a_later_metadata_batch(bad_id, kv):
+    """Waves of more than 64 blocks read their block ids in batches of 64;
+    an unmapped or out-of-range id in the second batch poisons its row only
+    (the id is checked where it is used, not where the batch is loaded)."""
+    c = make_case(7151, [3000, 2900, 64], n_q=8, n_kv=2, d_h=128, kv_dtype=kv)
+    t = c.table.copy()
+    t[0, 150] = bad_id              # block 150 of row 0: the second batch of its wave
+    _say(f"bad id {bad_id} in a later batch kv={kv}")
+    got, _ = run_case(c, table=t, num_partitions=3)
+    ref = c.oracle_out()
+    assert np.isnan(got[0]).all()
+    assert_parity(max_err(got[[1, 2]], ref[[1, 2]]), TOL_16BIT if kv == BF16 else TOL_8BIT)
+
+
 @pytest.mark.parametrize("parts", [0, 1, 4])
 def test_context_beyond_table_is_nan(parts):
     c = make_case(7201, [40, 20], n_q=4, n_kv=2, d_h=64, max_blocks=3)
