@@ -234,7 +234,7 @@ def _events(n):
             for _ in range(n)]
 
 
-def read_probe(dev, table, ctx, w, reps=10):
+def read_probe(dev, table, ctx, w, scratch, reps=10, sequential=True):
     """Read-only HBM probes (pda_hbm_read_probe), GB/s: a sequential walk of
     2 GiB (2048 waves), and the (block, head) K and V tiles of this workload
     read in the attention kernel's order (segment by segment, K then V per
@@ -242,7 +242,8 @@ def read_probe(dev, table, ctx, w, reps=10):
     caches, 2048 for 8-bit and 4-bit ones), from a buffer laid out like the
     two caches (the 4-bit value scales are not read). Each figure is the
     median of 5 runs of `reps` back-to-back launches between two HIP
-    events."""
+    events; the tile probe is also timed as the steps are, each run after a
+    1 GiB write of `scratch` (median of 20, `kv_tiles_flushed_*`)."""
     import torch
     import synth
     import decode_attention_paged_slot_amd as pda
@@ -263,12 +264,13 @@ def read_probe(dev, table, ctx, w, reps=10):
         return float(np.median(per))
 
     out = {}
-    seq_bytes = 2 << 30
-    buf = torch.empty(seq_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
-    sink = torch.empty(2048 * 64, dtype=torch.int32, device=dev)
-    ms = timed(pda.hbm_read_probe(buf, sink, waves=2048, bind=True))
-    out["sequential_GBps"] = round(seq_bytes / (ms * 1e-3) / 1e9, 1)
-    del buf
+    if sequential:
+        seq_bytes = 2 << 30
+        buf = torch.empty(seq_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
+        sink = torch.empty(2048 * 64, dtype=torch.int32, device=dev)
+        ms = timed(pda.hbm_read_probe(buf, sink, waves=2048, bind=True))
+        out["sequential_GBps"] = round(seq_bytes / (ms * 1e-3) / 1e9, 1)
+        del buf
     if w.kv_dtype in (synth.BF16, synth.FP8, synth.INT8, synth.INT4) and not w.attn_window:
         eb = synth.ELEM_BYTES[w.kv_dtype]
         waves = 1024 if w.kv_dtype == synth.BF16 else 2048
@@ -286,10 +288,14 @@ def read_probe(dev, table, ctx, w, reps=10):
         buf = torch.empty(2 * nb_pool * blk // 4, dtype=torch.int32, device=dev).fill_(1)
         t_off = torch.from_numpy(offs).to(dev)
         sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
-        ms = timed(pda.hbm_read_probe(buf, sink, tile_offsets=t_off, tile_bytes=tile, waves=waves,
-                                      bind=True))
+        call = pda.hbm_read_probe(buf, sink, tile_offsets=t_off, tile_bytes=tile, waves=waves,
+                                  bind=True)
+        ms = timed(call)
         out["kv_tiles_GBps"] = round(offs.size * tile / (ms * 1e-3) / 1e9, 1)
         out["kv_tiles_us"] = round(ms * 1e3, 2)
+        ms_f = float(np.median(flushed_calls(call, 20, scratch)))
+        out["kv_tiles_flushed_GBps"] = round(offs.size * tile / (ms_f * 1e-3) / 1e9, 1)
+        out["kv_tiles_flushed_us"] = round(ms_f * 1e3, 2)
         out["kv_tiles_bytes"] = int(offs.size * tile)
         del buf, t_off
     torch.cuda.empty_cache()
@@ -669,7 +675,10 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         extra = measure(synth.WORKLOADS[LONG_WORKLOAD], args, dev, K, scratch,
                         not args.no_oracle)
-    probe = None if args.no_probe else read_probe(dev, r["table"], r["inp_ctx"], w)
+    probe = None if args.no_probe else read_probe(dev, r["table"], r["inp_ctx"], w, scratch)
+    probe_long = (None if args.no_probe or extra is None else
+                  read_probe(dev, extra["table"], extra["inp_ctx"], extra["w"], scratch,
+                             sequential=False))
     del scratch
     torch.cuda.empty_cache()
 
@@ -678,14 +687,23 @@ def main(argv=None) -> int:
     achieved = r["att_bytes"] / (med_ms * 1e-3) / 1e9
     value = r["step_bytes"] / (med_ms * 1e-3) / 1e9
 
-    def summary(x):
+    def probe_pct(pr, rate):
+        """The step's rate against the tile probe's, back to back and flushed."""
+        if pr is None or "kv_tiles_GBps" not in pr:
+            return {}
+        return {"pct_of_kv_tiles": round(100.0 * rate / pr["kv_tiles_GBps"], 2),
+                "pct_of_kv_tiles_flushed": round(100.0 * rate / pr["kv_tiles_flushed_GBps"], 2)}
+
+    def summary(x, pr):
         wx = x["w"]
         return {"workload": wx.name, "us": x["us"], "GBps": x["GBps"],
                 "attention_GBps": x["attention_GBps"],
                 "frac": round(x["attention_GBps"] / HBM_PEAK_GBPS, 4),
                 "warm_attention_frac": round(x["warm_GBps"] / HBM_PEAK_GBPS, 4),
                 "bytes_attention": x["att_bytes"], "parity": x["parity"],
-                "traffic": measured_traffic(wx.name)}
+                "traffic": measured_traffic(wx.name),
+                **({} if pr is None else
+                   {"read_probe": {**pr, **probe_pct(pr, x["attention_GBps"])}})}
 
     cfg = {"workload": w.name, "B": w.B, "n_q": w.n_q, "n_kv": w.n_kv, "d_h": w.d_h,
            "block_size": w.block_size, "kv_dtype": synth.DTYPE_NAMES[w.kv_dtype],
@@ -731,11 +749,9 @@ def main(argv=None) -> int:
         **({} if probe is None else {
             "read_probe": {**probe,
                            "pct_of_sequential": round(100.0 * achieved / probe["sequential_GBps"], 2),
-                           **({} if "kv_tiles_GBps" not in probe else {
-                               "pct_of_kv_tiles": round(100.0 * achieved / probe["kv_tiles_GBps"],
-                                                        2)})}}),
+                           **probe_pct(probe, achieved)}}),
         **({} if "steady_state" not in r else {"steady_state": r["steady_state"]}),
-        **({} if extra is None else {"long_context": summary(extra)}),
+        **({} if extra is None else {"long_context": summary(extra, probe_long)}),
         "parity": r["parity"],
         "cpu_baseline": r["cpu"],
     }
