@@ -240,7 +240,9 @@ def read_probe(dev, table, ctx, w, scratch, reps=10, sequential=True):
     read in the attention kernel's order (segment by segment, K then V per
     block, four tiles in flight, with the kernel's wave count: 1024 for bf16
     caches, 2048 for 8-bit and 4-bit ones), from a buffer laid out like the
-    two caches (the 4-bit value scales are not read). Each figure is the
+    two caches (the 4-bit value scales are not read). A tile several rows
+    share (a shared prefix) is read once, where it first appears, so the
+    probe moves the unique bytes the steps are rated on. Each figure is the
     median of 5 runs of `reps` back-to-back launches between two HIP
     events; the tile probe is also timed as the steps are, each run after a
     1 GiB write of `scratch` (median of 20, `kv_tiles_flushed_*`)."""
@@ -279,8 +281,12 @@ def read_probe(dev, table, ctx, w, scratch, reps=10, sequential=True):
         nblk = synth.blocks_needed(ctx, w.block_size)
         nb_pool = int(table.max()) + 1
         offs = []
+        seen = np.zeros(nb_pool, bool)
         for b in range(w.B):
             ids = table[b, :nblk[b]].astype(np.int64)
+            ids = ids[ids >= 0]
+            ids = ids[~seen[ids]]
+            seen[ids] = True
             for j in range(w.n_kv):
                 k = ids * blk + j * tile
                 offs.append(np.stack([k, k + nb_pool * blk], 1).reshape(-1))
