@@ -712,10 +712,6 @@ __global__ void __launch_bounds__(kAttnThreads, KV == DT_BF16 ? 1 : 2) k_attn_mf
         }
         return t;
     };
-    auto meta_mask = [&](int i) {
-        const int v = (i >> 6) == batchA ? A.mask : Bm.mask;
-        return (uint32_t)__builtin_amdgcn_readlane(v, i & 63);
-    };
 
     // the consumed block always lies in batch A (the consumer moves to the
     // next batch first), so its fields need no batch select
