@@ -31,13 +31,24 @@ hipError_t launch_read_probe(const void*, size_t, const int64_t*, int64_t, int32
                              uint32_t*, hipStream_t) {
     return hipErrorNoDevice;
 }
-size_t attn_mfma_dyn_lds(int32_t B) { return (size_t)(3 * B + 2) * sizeof(int32_t); }
 
 }  // namespace pda
 
-extern "C" int32_t pda_paged_decode_attn_noalloc(const void*, const void*, const void*,
-                                                 const int32_t*, const int32_t*, float, void*,
-                                                 const pda_attn_desc*, void*) {
-    pda::set_error("host-only build: no device code");
-    return PDA_EHIP;
+// The allocation-free call without its per-device scratch array: a call that
+// needs workspace reports the missing device code; one that needs none (no
+// work, or an unsplit plan) goes on as in the library.
+extern "C" int32_t pda_paged_decode_attn_noalloc(const void* q, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_table,
+                                                 const int32_t* context_lens, float scale,
+                                                 void* out, const pda_attn_desc* d,
+                                                 void* stream) {
+    size_t need = 0;
+    const int32_t rc = pda_attn_workspace_size(d, &need);
+    if (rc != PDA_OK) return rc;
+    if (need > 0) {
+        pda::set_error("host-only build: no device code");
+        return PDA_EHIP;
+    }
+    return pda_paged_decode_attn(q, k_cache, v_cache, block_table, context_lens, scale, out, d,
+                                 nullptr, 0, stream);
 }

@@ -242,3 +242,47 @@ def test_int4_descriptor_rules():
     assert rc == binding.EINVAL
     rc = binding._lib.pda_kv_append_int4(*(None,) * 10, binding.ctypes.byref(d), None)
     assert rc == binding.EINVAL and "NULL" in pda.last_error()
+
+
+# entry points taking an attention descriptor: (name, kv dtype, prefix blocks,
+# fused new-row dtype); every pointer is NULL below
+_ZERO_WORK_CALLS = [
+    ("pda_paged_decode_attn", pda.BF16, 0), ("pda_paged_decode_attn_noalloc", pda.BF16, 0),
+    ("pda_paged_decode_attn_quant", pda.FP8_E4M3, 0), ("pda_decode_step", pda.BF16, 0),
+    ("pda_decode_step_quant", pda.INT8, 0), ("pda_paged_decode_attn_prefix", pda.FP8_E4M3, 4),
+    ("pda_decode_step_prefix", pda.FP8_E4M3, 4), ("pda_kv_append_int4", pda.INT4, 0),
+    ("pda_paged_decode_attn_int4", pda.INT4, 0), ("pda_decode_step_int4", pda.INT4, 0),
+]
+
+
+@pytest.mark.parametrize("name,kv,prefix", _ZERO_WORK_CALLS)
+def test_zero_work_returns_ok_and_runs_nothing(name, kv, prefix):
+    """A request with no work (B = 0, or no tokens to append) returns OK with
+    every pointer NULL. Without a GPU here, any HIP call would have failed the
+    call, so OK also shows that nothing was launched. With B > 0 the same
+    call fails (the NULL pointers, or for the allocation-free call the
+    missing device, whose scratch it resolves first)."""
+    fn = getattr(binding._lib, name)
+    for B in (0, 2):
+        d = _desc(B=B, kv_dtype=kv, prefix_blocks=prefix,
+                  new_dtype=pda.BF16 if kv in (pda.BF16, pda.INT4) else pda.F32)
+        args = []
+        for t in fn.argtypes:
+            if t is binding.ctypes.c_float:
+                args.append(1.0)
+            elif t is binding.ctypes.c_size_t:
+                args.append(0)
+            elif t is binding.ctypes.POINTER(pda.AttnDesc):
+                args.append(binding.ctypes.byref(d))
+            else:
+                args.append(None)
+        rc = fn(*args)
+        assert (rc == binding.OK) == (B == 0), (name, B, rc, pda.last_error())
+
+
+def test_zero_tokens_quantized_append():
+    kd = pda.KvDesc(2, 128, 16, 10, pda.FP8_E4M3, pda.BF16)
+    assert binding._lib.pda_kv_append_quant(None, None, None, 0, None, None, None, None,
+                                            binding.ctypes.byref(kd), None) == binding.OK
+    assert binding._lib.pda_kv_append_quant(None, None, None, 1, None, None, None, None,
+                                            binding.ctypes.byref(kd), None) == binding.EINVAL
