@@ -285,12 +285,17 @@ int32_t check_attn_desc(const pda_attn_desc* d, CallKind kind) {
         set_error("q_dtype / out_dtype must be F32 or BF16");
         return PDA_EINVAL;
     }
+    // The stream kernel indexes its block axis (n_kv segments per row, each
+    // up to max_blocks_per_seq blocks, plus a 4-bit cache's pad block and the
+    // split units charged per segment) in 32 bits.
     if (d->kv_dtype != PDA_F32 &&
         (d->B > kMaxStreamBatch ||
-         (int64_t)d->B * d->n_kv * d->max_blocks_per_seq >= ((int64_t)1 << 31) ||
+         (int64_t)d->B * d->n_kv * ((int64_t)d->max_blocks_per_seq + 1 + kMaxSegCost) >=
+             ((int64_t)1 << 31) ||
          (int64_t)d->B * d->n_kv >= ((int64_t)1 << 24))) {
-        set_error("batch too large for one call: B <= %d and B * n_kv * max_blocks_per_seq < 2^31",
-                  kMaxStreamBatch);
+        set_error("batch too large for one call: B <= %d and "
+                  "B * n_kv * (max_blocks_per_seq + %d) < 2^31",
+                  kMaxStreamBatch, 1 + kMaxSegCost);
         return PDA_EINVAL;
     }
     if ((int64_t)d->B * d->max_blocks_per_seq > INT32_MAX ||
@@ -462,7 +467,7 @@ int32_t run_attn(const void* q, const void* k_cache, const void* v_cache, const 
     // and a wave crossing dozens of such segments set the kernel's time until
     // each segment start was charged as 4 blocks; with whole rows the
     // segments are long and equal block counts per wave are best.
-    a.seg_cost = std::max(env_int("PDA_SEGMENT_COST", prefix ? 4 : 0), 0);
+    a.seg_cost = std::min(std::max(env_int("PDA_SEGMENT_COST", prefix ? 4 : 0), 0), kMaxSegCost);
     a.prefix_table = prefix ? prefix_table : nullptr;
     a.prefix_lens = prefix ? prefix_lens : nullptr;
     a.prefix_blocks = prefix ? d->prefix_blocks : 0;

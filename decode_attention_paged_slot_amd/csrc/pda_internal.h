@@ -107,6 +107,7 @@ constexpr int kBlockSize = 16;
 constexpr int kMaxPartitions = 2048;
 constexpr int kMaxStreamBatch = 4096;      // sequences per call on the stream plan (LDS prefix)
 constexpr int kMaxStreamWaves = 8192;      // wave ranges on the stream plan (merge LDS)
+constexpr int kMaxSegCost = 64;            // split units charged per segment, at most
 constexpr int kAttnThreads = 256;
 constexpr int kPrefixChunk = 16;           // shared-prefix blocks per prefix-pass workgroup
 constexpr int kMaxPrefixBlocks = 32768;    // shared-prefix blocks per call (merge LDS)

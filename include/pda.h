@@ -254,7 +254,9 @@ int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
  * Row semantics: n == 0 -> zero row. A logical block whose table entry is
  * outside [0, num_blocks), or n < 0, or n > max_blocks_per_seq * bs, is an
  * error (the worked example's failing lookup): that row's output is NaN.
- * Rows may share physical blocks (read-only aliasing). Errors: EINVAL,
+ * Rows may share physical blocks (read-only aliasing). One call takes at
+ * most 4096 sequences (16-bit, 8-bit and 4-bit caches) with
+ * B * n_kv * (max_blocks_per_seq + 65) < 2^31 (EINVAL beyond). Errors: EINVAL,
  * EWORKSPACE, EHIP. With PDA_DEBUG=1 in the environment the host also copies
  * block_table / context_lens back (synchronising `stream`) and returns EINVAL
  * for any such row before launching. It checks the blocks the call looks up,
@@ -273,7 +275,7 @@ int32_t pda_attn_plan(const pda_attn_desc* d, int32_t* num_partitions,
  *                            split shrinks the wave count (default 8)
  *   PDA_SEGMENT_COST         extra units charged per (sequence, KV head)
  *                            segment when ranges are cut (default 0; 4 for
- *                            the _prefix calls) */
+ *                            the _prefix calls; at most 64) */
 int32_t pda_paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* context_lens, float scale,
                               void* out, const pda_attn_desc* d, void* workspace,

@@ -286,3 +286,22 @@ def test_zero_tokens_quantized_append():
                                             binding.ctypes.byref(kd), None) == binding.OK
     assert binding._lib.pda_kv_append_quant(None, None, None, 1, None, None, None, None,
                                             binding.ctypes.byref(kd), None) == binding.EINVAL
+
+
+def test_block_axis_limit_leaves_room_for_pad_and_segment_units():
+    """The stream kernel indexes its block axis in 32 bits: B * n_kv segments
+    of up to max_blocks_per_seq blocks, plus one pad block (4-bit cache) and
+    up to 64 split units per segment. A descriptor whose bare block count
+    fits under 2^31 but whose axis with that margin does not is refused."""
+    B, n_kv = 4096, 8
+    ok = (1 << 31) // (B * n_kv) - 65 - 1          # the largest max_blocks_per_seq accepted
+    d = _desc(B=B, n_q=n_kv, n_kv=n_kv, max_blocks_per_seq=ok, num_blocks=1000)
+    size = binding.ctypes.c_size_t()
+    assert binding._lib.pda_attn_workspace_size(binding.ctypes.byref(d),
+                                                binding.ctypes.byref(size)) == binding.OK
+    for mb in (ok + 1, (1 << 31) // (B * n_kv) - 1):   # the second fits without the margin
+        d = _desc(B=B, n_q=n_kv, n_kv=n_kv, max_blocks_per_seq=mb, num_blocks=1000)
+        assert B * n_kv * mb < (1 << 31)
+        assert binding._lib.pda_attn_workspace_size(binding.ctypes.byref(d),
+                                                    binding.ctypes.byref(size)) == binding.EINVAL
+        assert "2^31" in pda.last_error()
