@@ -305,3 +305,38 @@ def test_block_axis_limit_leaves_room_for_pad_and_segment_units():
         assert binding._lib.pda_attn_workspace_size(binding.ctypes.byref(d),
                                                     binding.ctypes.byref(size)) == binding.EINVAL
         assert "2^31" in pda.last_error()
+
+
+@pytest.mark.parametrize("name,kv,prefix", [
+    ("pda_paged_decode_attn", pda.BF16, 0), ("pda_paged_decode_attn_quant", pda.FP8_E4M3, 0),
+    ("pda_paged_decode_attn_int4", pda.INT4, 0), ("pda_paged_decode_attn_prefix", pda.INT8, 4)])
+def test_short_workspace_is_refused_before_any_launch(name, kv, prefix):
+    """A split plan needs a workspace of pda_attn_workspace_size bytes: one
+    byte less, none, or a misaligned one is EWORKSPACE, decided on the host
+    before anything is launched (the device pointers are never touched, so
+    placeholder addresses do here)."""
+    d = _desc(B=8, n_q=64, n_kv=8, max_blocks_per_seq=2048, num_blocks=20000, kv_dtype=kv,
+              max_context=32768, total_context=8 * 32768, prefix_blocks=prefix)
+    need = binding.ctypes.c_size_t()
+    assert binding._lib.pda_attn_workspace_size(binding.ctypes.byref(d),
+                                                binding.ctypes.byref(need)) == binding.OK
+    assert need.value > 0
+    fn = getattr(binding._lib, name)
+    fake = 1 << 20                                  # 16-byte aligned, never dereferenced
+    for ws, nbytes in ((fake, need.value - 1), (None, need.value), (fake + 8, need.value)):
+        args = []
+        for t in fn.argtypes:
+            if t is binding.ctypes.c_float:
+                args.append(0.125)
+            elif t is binding.ctypes.POINTER(pda.AttnDesc):
+                args.append(binding.ctypes.byref(d))
+            else:
+                args.append(None)
+        # pointers in order; the workspace, its size and the stream are the last three
+        ptrs = [i for i, t in enumerate(fn.argtypes[:-3])
+                if t not in (binding.ctypes.c_float, binding.ctypes.POINTER(pda.AttnDesc))]
+        for i in ptrs:
+            args[i] = fake
+        args[-3], args[-2], args[-1] = ws, nbytes, None
+        assert fn(*args) == binding.EWORKSPACE, (name, ws, nbytes, pda.last_error())
+        assert "workspace" in pda.last_error()
