@@ -340,3 +340,52 @@ def test_short_workspace_is_refused_before_any_launch(name, kv, prefix):
         args[-3], args[-2], args[-1] = ws, nbytes, None
         assert fn(*args) == binding.EWORKSPACE, (name, ws, nbytes, pda.last_error())
         assert "workspace" in pda.last_error()
+
+
+def _call_with(fn, d, ptr, scale, override=None):
+    """Arguments for an attention / step entry point: every pointer `ptr`,
+    the float `scale`, descriptor `d`, no workspace; `override` maps a
+    parameter index to a value."""
+    args = []
+    for t in fn.argtypes:
+        if t is binding.ctypes.c_float:
+            args.append(scale)
+        elif t is binding.ctypes.c_size_t:
+            args.append(0)
+        elif t is binding.ctypes.POINTER(pda.AttnDesc):
+            args.append(binding.ctypes.byref(d))
+        else:
+            args.append(ptr)
+    args[-1] = None   # stream
+    args[-3] = None   # workspace
+    for i, v in (override or {}).items():
+        args[i] = v
+    return fn(*args)
+
+
+def test_bad_scale_alignment_and_new_row_dtype_are_refused_before_any_launch():
+    """The other host-side refusals of the attention calls, with placeholder
+    device addresses that are never touched: a non-finite scale, a buffer not
+    16-byte aligned, and a fused step whose new rows are not in the cache's
+    dtype (16-bit caches) or in F32 / BF16 (8-bit caches)."""
+    fake = 1 << 20
+    d = _desc(B=2, max_context=100)   # short rows: an unsplit plan, no workspace
+    fn = binding._lib.pda_paged_decode_attn
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert _call_with(fn, d, fake, bad) == binding.EINVAL
+        assert "scale" in pda.last_error()
+    for i in (0, 1, 2, 6):                        # q, k_cache, v_cache, out
+        assert _call_with(fn, d, fake, 0.1, {i: fake + 8}) == binding.EINVAL
+        assert "aligned" in pda.last_error()
+    step = binding._lib.pda_decode_step
+    assert _call_with(step, _desc(B=2, max_context=100, new_dtype=pda.F32), fake,
+                      0.1) == binding.EINVAL
+    assert "new_dtype" in pda.last_error()
+    step_q = binding._lib.pda_decode_step_quant
+    assert _call_with(step_q, _desc(B=2, max_context=100, kv_dtype=pda.FP8_E4M3,
+                                    new_dtype=pda.INT8), fake, 0.1) == binding.EINVAL
+    assert "new_dtype" in pda.last_error()
+    # k_new / v_new of a fused step must be aligned as well
+    assert _call_with(step, _desc(B=2, max_context=100), fake, 0.1,
+                      {1: fake + 4}) == binding.EINVAL
+    assert "k_new" in pda.last_error()
