@@ -389,3 +389,14 @@ def test_bad_scale_alignment_and_new_row_dtype_are_refused_before_any_launch():
     assert _call_with(step, _desc(B=2, max_context=100), fake, 0.1,
                       {1: fake + 4}) == binding.EINVAL
     assert "k_new" in pda.last_error()
+
+
+def test_binding_refuses_host_tensors():
+    """The Python binding checks every tensor before the C call; a host
+    tensor's address is not a device pointer, so the call is refused (the
+    dtype, shape and contiguity checks are run on the GPU)."""
+    import torch
+    k = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16)
+    kn = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        pda.kv_append(kn, kn.clone(), torch.zeros(3, dtype=torch.int64), k, k.clone())
